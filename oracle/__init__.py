@@ -1,0 +1,123 @@
+"""fp64 CPU oracle for 2D Neighborhood Attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline leg
+of ``bench.py`` may import this package.  The product library never loads it
+and shares no code with it.
+
+The arithmetic lives in ``na2d_oracle.c`` (plain loops, double precision,
+OpenMP over rows); this module only builds and calls it.  Definition: the NA
+equations 2-4 of "Neighborhood Attention Transformer" (CSDN translation,
+section 3.1), with the per-axis clamped window of section 1 / section 3.1 and
+the qiita article's border figure.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "na2d_oracle.c")
+LIBRARY = os.path.join(_HERE, "libna2d_oracle.so")
+
+
+def compile_oracle(src: str, out: str) -> str:
+    """Compile an oracle source with gcc (OpenMP, -O2, no fast-math, no FMA contraction)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(LIBRARY):
+        compile_oracle(SOURCE, LIBRARY)
+    return LIBRARY
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes front of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.na2d_oracle_window_start.argtypes = [I, I, I]
+        lib.na2d_oracle_window_start.restype = I
+        lib.na2d_oracle_f64.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I]
+        lib.na2d_oracle_f64.restype = I
+        lib.na2d_oracle_f64_sampled.argtypes = [P, P, P, P, P, I64, P, I, I, I, I, I, I, I]
+        lib.na2d_oracle_f64_sampled.restype = I
+        self.lib = lib
+        self.path = path
+
+    def window_start(self, i: int, k: int, L: int) -> int:
+        """Start of the clamped window of size k around index i on an axis of length L."""
+        return self.lib.na2d_oracle_window_start(i, k, L)
+
+    def na2d_forward(self, q, k, v, rpb, ksize: int, nthreads: int = 0) -> np.ndarray:
+        """NA2D forward.  q, k, v: [B, heads, H, W, d]; rpb: [heads, 2k-1, 2k-1] or None."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        assert q.ndim == 5 and q.shape == k.shape == v.shape
+        B, heads, H, W, d = q.shape
+        if rpb is not None:
+            rpb = _f64(rpb)
+            assert rpb.shape == (heads, 2 * ksize - 1, 2 * ksize - 1)
+        out = np.empty_like(q)
+        rc = self.lib.na2d_oracle_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(out),
+                                      B, heads, H, W, d, ksize, nthreads)
+        if rc != 0:
+            raise ValueError("oracle rejected sizes B=%d heads=%d H=%d W=%d d=%d k=%d"
+                             % (B, heads, H, W, d, ksize))
+        return out
+
+    def na2d_forward_sampled(self, q, k, v, rpb, ksize: int, idx, nthreads: int = 0):
+        """Outputs [n, d] for the queries with linear index ((b*heads+h)*H+y)*W+x."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, heads, H, W, d = q.shape
+        if rpb is not None:
+            rpb = _f64(rpb)
+            assert rpb.shape == (heads, 2 * ksize - 1, 2 * ksize - 1)
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        out = np.empty((idx.size, d), dtype=np.float64)
+        rc = self.lib.na2d_oracle_f64_sampled(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(idx),
+                                              idx.size, _ptr(out), B, heads, H, W, d, ksize,
+                                              nthreads)
+        if rc != 0:
+            raise ValueError("oracle rejected the request")
+        return out
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def window_start(i: int, k: int, L: int) -> int:
+    return default().window_start(i, k, L)
+
+
+def na2d_forward(q, k, v, rpb, ksize: int, nthreads: int = 0) -> np.ndarray:
+    return default().na2d_forward(q, k, v, rpb, ksize, nthreads)
+
+
+def na2d_forward_sampled(q, k, v, rpb, ksize: int, idx, nthreads: int = 0) -> np.ndarray:
+    return default().na2d_forward_sampled(q, k, v, rpb, ksize, idx, nthreads)
