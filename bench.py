@@ -1,0 +1,215 @@
+"""Benchmark of the fused NA2D forward on one MI355X.
+
+One step = one fused NA2D forward launch over the whole batch of the
+NAT-Tiny stage-1 workload (B=32, 2 heads, 56x56, d=32, k=7, fp16 inputs,
+fp32 output), inputs already resident in HBM.  The timed region rotates over
+enough input/output sets (>= 1 GiB) that the 256 MB Infinity Cache cannot hold
+them, so the figure is an HBM figure.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|valu|mfma]
+
+``--gpus N`` with N > 1 is refused: this build measures one GPU (the op
+shards over (batch, head) maps with no communication at all).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NA2D fwd queries/s and achieved HBM GB/s (% roofline), NAT-Tiny stage1 k=7"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
+KERNEL_SOURCES = {1: "na2d_valu.hip", 2: "na2d_mfma.hip"}
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes the op itself must move: read q, k, v once, write fp32 out once,
+    read the bias table once per head (halo re-reads are not counted)."""
+    es = 4 if w.dtype == "f32" else 2
+    per_query = 3 * w.d * es + 4 * w.d
+    return w.queries * per_query + w.heads * (2 * w.k - 1) ** 2 * 4
+
+
+def algorithmic_flops(w) -> int:
+    """QK and AV: 2 * k^2 * d multiply-adds per query, a multiply-add = 2 flops."""
+    return w.queries * 4 * w.k * w.k * w.d
+
+
+def source_digest(name: str) -> str:
+    path = os.path.join(ROOT, "vision_sliding_window_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str, algo_name: str, kernel_src: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the kernel source as it is now (else None)."""
+    path = os.path.join(ROOT, "profiles", "na2d_%s_%s_traffic.txt" % (algo_name, workload))
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, _, val = line.partition(":")
+                vals[key.strip()] = val.strip()
+    try:
+        if vals.get("kernel_source_sha256_16") != source_digest(kernel_src):
+            return None
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x, seconds: float = 10.0):
+    """The fp64 oracle as it stands, on the host cores, on a bounded sample of
+    the same workload: as many passes over a random sample of queries as fit in
+    about `seconds`."""
+    import numpy as np
+    import oracle
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        cores = min(cores, int(env))
+    rng = np.random.default_rng(1)
+    probe = rng.choice(w.queries, size=min(w.queries, 4096), replace=False)
+    t0 = time.perf_counter()
+    oracle.na2d_forward_sampled(x.q64, x.k64, x.v64, x.rpb64, w.k, probe, nthreads=cores)
+    rate = probe.size / max(time.perf_counter() - t0, 1e-6)
+    n = int(min(w.queries, max(probe.size, rate * seconds)))
+    sample = rng.choice(w.queries, size=n, replace=False)
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        oracle.na2d_forward_sampled(x.q64, x.k64, x.v64, x.rpb64, w.k, sample, nthreads=cores)
+        done += n
+        el = time.perf_counter() - t0
+        if el >= seconds * 0.8 or done >= 8 * w.queries:
+            break
+    return {"value": done / el, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": "%d random queries of %s (seed 1), %d pass(es), fp64, %.1f s"
+                      % (n, w.name, done // n, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--algo", default="auto", choices=sorted(ALGOS))
+    ap.add_argument("--min-footprint-gib", type=float, default=1.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the NA2D forward shards over (batch, head) "
+              "maps with no communication, so N > 1 is not run here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from vision_sliding_window_amd import na2d
+    from vision_sliding_window_amd.inputs import BENCH_WORKLOAD, WORKLOADS, workload_inputs
+
+    wname = args.workload or BENCH_WORKLOAD
+    w = WORKLOADS[wname]
+    lib = na2d.load()  # raises if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dtype_code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
+    algo = ALGOS[args.algo]
+    if algo == 0:
+        algo = na2d.na2d_select_algo(w.H, w.W, w.d, w.k, dtype_code)
+    algo_name = {1: "valu", 2: "mfma"}[algo]
+
+    x = workload_inputs(w, seed=0)
+    set_bytes = algorithmic_bytes(w)
+    nsets = max(1, math.ceil(args.min_footprint_gib * 2 ** 30 / set_bytes))
+    q0, k0, v0 = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    rpb = x.rpb.to(dev)
+    sets = []
+    for i in range(nsets):
+        sets.append((q0.clone() if i else q0, k0.clone() if i else k0, v0.clone() if i else v0,
+                     torch.empty(w.shape, dtype=torch.float32, device=dev)))
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def launch(i):
+        q, k, v, out = sets[i % nsets]
+        st = lib.na2d_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
+                                 out.data_ptr(), w.B, w.heads, w.H, w.W, w.d, w.k, dtype_code,
+                                 algo, sptr)
+        if st != 0:
+            raise RuntimeError("na2d_forward_ex failed: %s" % na2d.na2d_strerror(st))
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # hot-cache figure (one set, L2/MALL resident), labelled as such
+    q, k, v, out = sets[0]
+    hs = torch.cuda.Event(enable_timing=True)
+    he = torch.cuda.Event(enable_timing=True)
+    hs.record(stream)
+    for _ in range(args.steps):
+        launch(0)
+    he.record(stream)
+    torch.cuda.synchronize()
+    hot_ms = hs.elapsed_time(he) / args.steps
+
+    value = w.queries / (ms * 1e-3)
+    gbs = set_bytes / (ms * 1e-3) / 1e9
+    tflops = algorithmic_flops(w) / (ms * 1e-3) / 1e12
+    traffic = read_traffic(wname, algo_name, KERNEL_SOURCES[algo])
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else int(traffic)}
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: Q,K,V ~ N(0,1), RPB ~ N(0,0.02), seed 0",
+        "config": {"workload": wname, "B": w.B, "heads": w.heads, "H": w.H, "W": w.W, "d": w.d,
+                   "k": w.k, "kernel": algo_name, "rotating_sets": nsets,
+                   "footprint_bytes": nsets * set_bytes, "algorithmic_bytes_per_step": set_bytes,
+                   "hot_ms_per_step": round(hot_ms, 6),
+                   "useful_tflops": round(tflops, 2)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

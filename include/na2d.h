@@ -1,0 +1,117 @@
+/*
+ * na2d.h -- C ABI of the fused 2D Neighborhood Attention forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is Neighborhood Attention as defined in "Neighborhood
+ * Attention Transformer" (CSDN translation of the CVPR 2023 paper, section
+ * 3.1, equations 2-4; restated in the qiita article "NAT:
+ * スライディングウィンドウアテンションの革新", section "Neighborhood
+ * Attention(NA)").  For every pixel (y, x) of an H x W map, every head h and
+ * every batch item b:
+ *
+ *   sy = clamp(y - ksize/2, 0, H - ksize),  sx = clamp(x - ksize/2, 0, W - ksize)
+ *   for the ksize*ksize keys (ky, kx) in [sy, sy+ksize) x [sx, sx+ksize):
+ *     logit = (q[b,h,y,x,:] . k[b,h,ky,kx,:] + rpb[h, ky-y+ksize-1, kx-x+ksize-1]) / sqrt(d)
+ *   out[b,h,y,x,:] = sum over keys of softmax(logit) * v[b,h,ky,kx,:]
+ *
+ * The window is the per-axis set of the ksize nearest pixels, pushed inward
+ * at the borders so every pixel keeps the same span (CSDN page, section 1 and
+ * section 3.1; qiita border figure).  The bias is divided by sqrt(d) together
+ * with Q.K, as Eq. 4 writes it.  No ksize*ksize attention tensor is written
+ * to memory: the logits, the softmax and the weighted sum stay on chip.
+ *
+ * Conventions shared by every entry point:
+ *  - q, k, v, out: device memory, [B, heads, H, W, d] contiguous, d fastest.
+ *    q, k, v hold `dtype` elements; out is always float32 (a 16-bit output
+ *    could not hold the result to the accuracy the fp32 accumulation gives).
+ *  - rpb: device memory, float32 [heads, 2*ksize-1, 2*ksize-1], indexed by the
+ *    key-minus-query offset (row, then column) plus ksize-1.  rpb == NULL
+ *    means no positional bias.
+ *  - All pointers must be 16-byte aligned; out must not overlap q, k, v or rpb.
+ *  - The caller owns every buffer.  The library allocates nothing, frees
+ *    nothing and never synchronises; it keeps no state, so concurrent calls
+ *    from several threads are safe.
+ *  - The call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Arguments are checked on the host before anything is
+ *    launched: an invalid call returns a negative status and launches
+ *    nothing.  A failed launch returns NA2D_ERR_HIP; na2d_last_error() then
+ *    gives the HIP error text for the calling thread.
+ *  - Non-finite inputs propagate; they are not checked.
+ */
+#ifndef NA2D_H
+#define NA2D_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k and v. */
+typedef enum {
+    NA2D_F32 = 0,
+    NA2D_F16 = 1,
+    NA2D_BF16 = 2
+} na2d_dtype;
+
+/* Kernel family.  AUTO picks MFMA for 16-bit inputs with d = 32 and
+ * 3 <= ksize <= NA2D_MFMA_MAX_KSIZE, the VALU kernel otherwise. */
+typedef enum {
+    NA2D_ALGO_AUTO = 0,
+    NA2D_ALGO_VALU = 1, /* one query per lane, fp32 arithmetic, any dtype       */
+    NA2D_ALGO_MFMA = 2  /* query tile x key/value halo in LDS, matrix cores      */
+} na2d_algo;
+
+/* Status codes (0 = success). */
+enum {
+    NA2D_OK = 0,
+    NA2D_ERR_NULL = -1,        /* q, k, v or out is NULL                                  */
+    NA2D_ERR_SHAPE = -2,       /* B, heads, H, W or d <= 0, or an element count overflows */
+    NA2D_ERR_KSIZE = -3,       /* ksize even, < 1, > H or > W                              */
+    NA2D_ERR_DTYPE = -4,       /* dtype not one of na2d_dtype                              */
+    NA2D_ERR_UNSUPPORTED = -5, /* d or ksize outside what the chosen kernel supports       */
+    NA2D_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                         */
+    NA2D_ERR_ALIAS = -7,       /* out overlaps q, k, v or rpb                              */
+    NA2D_ERR_HIP = -8,         /* the HIP runtime reported an error at launch              */
+    NA2D_ERR_ALGO = -9         /* algo not one of na2d_algo                                */
+};
+
+/* Largest ksize each kernel family accepts.  d must be 16, 32, 64 or 128 for
+ * the VALU kernel and 32 for the MFMA kernel. */
+#define NA2D_VALU_MAX_KSIZE 63
+#define NA2D_MFMA_MAX_KSIZE 25
+
+/* Fused NA2D forward (CSDN page, section 3.1, Eq. 2-4), kernel chosen
+ * automatically.  Sizes are element counts; see the conventions above. */
+int na2d_forward(const void *q, const void *k, const void *v, const float *rpb, float *out,
+                 int B, int heads, int H, int W, int d, int ksize, int dtype, void *stream);
+
+/* The same operation with the kernel family forced by `algo` (na2d_algo).
+ * NA2D_ERR_UNSUPPORTED if that family cannot run these sizes or dtype. */
+int na2d_forward_ex(const void *q, const void *k, const void *v, const float *rpb, float *out,
+                    int B, int heads, int H, int W, int d, int ksize, int dtype, int algo,
+                    void *stream);
+
+/* Host-only argument check: the status na2d_forward_ex would return for these
+ * arguments before launching, with no HIP call made.  Pointers are only
+ * compared, never dereferenced. */
+int na2d_check_args(const void *q, const void *k, const void *v, const float *rpb,
+                    const float *out, int B, int heads, int H, int W, int d, int ksize,
+                    int dtype, int algo);
+
+/* The kernel family AUTO resolves to for these sizes (NA2D_ALGO_VALU or
+ * NA2D_ALGO_MFMA), or a negative status if the sizes are invalid. */
+int na2d_select_algo(int H, int W, int d, int ksize, int dtype);
+
+/* Static text for a status code. */
+const char *na2d_strerror(int status);
+
+/* Detail of the last NA2D_ERR_HIP on the calling thread ("" if none). */
+const char *na2d_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int na2d_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NA2D_H */

@@ -1,0 +1,117 @@
+"""GPU path vs the fp64 oracle, element by element, on small and ragged maps.
+
+Tolerances (max-abs over every output element): 1e-5 for float32 inputs,
+2e-3 for fp16/bf16 inputs with fp32 accumulation.  Every case runs through
+the C ABI (ctypes binding), once per kernel family that supports it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from vision_sliding_window_amd import na2d
+from vision_sliding_window_amd.inputs import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+VALU, MFMA = na2d.NA2D_ALGO_VALU, na2d.NA2D_ALGO_MFMA
+
+
+def gpu_forward(x, ks, algo, with_bias=True):
+    dev = torch.device("cuda")
+    rpb = x.rpb.to(dev) if with_bias else None
+    out = na2d.forward(x.q.to(dev), x.k.to(dev), x.v.to(dev), rpb, ks, algo=algo)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy()
+
+
+def check(shape, ks, dtype, algo, seed=0, with_bias=True, **kw):
+    print("case", shape, ks, dtype, algo, kw, flush=True)
+    x = make_inputs(shape, ks, dtype, seed=seed, **kw)
+    got = gpu_forward(x, ks, algo, with_bias)
+    want = oracle.na2d_forward(x.q64, x.k64, x.v64, x.rpb64 if with_bias else None, ks)
+    err = np.abs(got - want).max()
+    assert np.isfinite(got).all()
+    assert err <= TOL[dtype], "max|err| %.3g > %.3g for %s k=%d %s algo=%d" % (
+        err, TOL[dtype], shape, ks, dtype, algo)
+    return err
+
+
+# (shape [B, heads, H, W, d], ksize)
+RAGGED = [
+    ((1, 1, 14, 14, 32), 7),    # the tiny workload
+    ((1, 1, 7, 7, 32), 7),      # k = H = W: full self attention
+    ((1, 3, 13, 29, 32), 3),
+    ((1, 2, 13, 29, 32), 5),
+    ((2, 2, 57, 55, 32), 7),    # several tiles plus ragged tails
+    ((1, 1, 7, 30, 32), 7),     # H = k < W
+    ((1, 1, 31, 7, 32), 7),     # W = k < H
+    ((1, 2, 13, 29, 32), 9),
+    ((1, 2, 13, 29, 32), 11),
+    ((2, 1, 29, 37, 32), 13),
+    ((1, 1, 23, 33, 32), 15),
+    ((1, 1, 21, 21, 32), 21),   # k = H = W at k = 21
+    ((1, 2, 45, 38, 32), 21),
+    ((1, 1, 25, 40, 32), 25),
+    ((1, 1, 3, 3, 32), 3),
+]
+
+
+@pytest.mark.parametrize("shape,ks", RAGGED, ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_mfma_ragged(shape, ks, dtype):
+    check(shape, ks, dtype, MFMA)
+
+
+@pytest.mark.parametrize("shape,ks", RAGGED, ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_valu_ragged(shape, ks, dtype):
+    check(shape, ks, dtype, VALU)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_valu_head_dims(dtype, d):
+    check((1, 2, 11, 13, d), 5, dtype, VALU)
+
+
+@pytest.mark.parametrize("algo", [VALU, MFMA])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_stress_bias_and_peaked(algo, dtype):
+    """RPB ~ N(0, 1) (the default 0.02 moves outputs by less than the tolerance)
+    and Q scaled by 4 (peaked softmax)."""
+    check((2, 2, 30, 26, 32), 7, dtype, algo, rpb_std=1.0)
+    check((2, 2, 30, 26, 32), 7, dtype, algo, q_scale=4.0)
+    check((1, 2, 40, 40, 32), 13, dtype, algo, rpb_std=1.0, q_scale=2.0)
+
+
+@pytest.mark.parametrize("algo", [VALU, MFMA])
+def test_no_bias(algo):
+    check((2, 2, 20, 24, 32), 7, "f16", algo, with_bias=False)
+
+
+def test_valu_f32_stress():
+    check((1, 2, 19, 17, 32), 7, "f32", VALU, rpb_std=1.0, q_scale=3.0)
+    check((1, 1, 16, 16, 32), 1, "f32", VALU)
+
+
+def test_k1_identity():
+    """k = 1: every query attends to itself only, so out = V exactly."""
+    x = make_inputs((2, 2, 9, 10, 32), 1, "f16", seed=3)
+    got = gpu_forward(x, 1, VALU)
+    assert np.array_equal(got, x.v64)
+
+
+@pytest.mark.parametrize("algo", [VALU, MFMA])
+def test_deterministic(algo):
+    x = make_inputs((4, 2, 56, 56, 32), 7, "f16", seed=5)
+    a = gpu_forward(x, 7, algo)
+    b = gpu_forward(x, 7, algo)
+    assert np.array_equal(a, b)
+
+
+def test_auto_selects_mfma_for_16bit():
+    assert na2d.na2d_select_algo(56, 56, 32, 7, na2d.NA2D_F16) == MFMA
+    assert na2d.na2d_select_algo(56, 56, 32, 7, na2d.NA2D_F32) == VALU
+    assert na2d.na2d_select_algo(56, 56, 64, 7, na2d.NA2D_BF16) == VALU

@@ -1,0 +1,21 @@
+// na2d_launch.h -- internal interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace na2d {
+
+// One validated forward problem (see include/na2d.h for the meaning of each field).
+struct Problem {
+    const void *q, *k, *v;
+    const float *rpb;  // may be null: no positional bias
+    float *out;
+    int B, heads, H, W, d, ksize, dtype;
+};
+
+// Launchers; each returns the HIP status of its launch.  The arguments have
+// been checked by the caller.
+hipError_t launch_valu(const Problem &p, hipStream_t stream);
+hipError_t launch_mfma(const Problem &p, hipStream_t stream);
+
+}  // namespace na2d

@@ -1,0 +1,150 @@
+"""Python binding of libna2d.so (C ABI in include/na2d.h): argument marshalling only.
+
+The functions named like the C entry points take raw device pointers (ints)
+or torch tensors (their ``data_ptr()`` is passed) and return the C status.
+``forward`` is a convenience that allocates the fp32 output with torch and
+raises on a non-zero status.  Every step of the attention runs in the HIP
+library; if it is missing this module raises on first use -- there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libna2d.so")
+
+NA2D_F32, NA2D_F16, NA2D_BF16 = 0, 1, 2
+NA2D_ALGO_AUTO, NA2D_ALGO_VALU, NA2D_ALGO_MFMA = 0, 1, 2
+NA2D_OK = 0
+NA2D_ERR_NULL = -1
+NA2D_ERR_SHAPE = -2
+NA2D_ERR_KSIZE = -3
+NA2D_ERR_DTYPE = -4
+NA2D_ERR_UNSUPPORTED = -5
+NA2D_ERR_ALIGN = -6
+NA2D_ERR_ALIAS = -7
+NA2D_ERR_HIP = -8
+NA2D_ERR_ALGO = -9
+
+EXPORTS = ["na2d_forward", "na2d_forward_ex", "na2d_check_args", "na2d_select_algo",
+           "na2d_strerror", "na2d_last_error", "na2d_version"]
+
+TORCH_DTYPE_CODE = {torch.float32: NA2D_F32, torch.float16: NA2D_F16, torch.bfloat16: NA2D_BF16}
+
+_lib = None
+
+
+class NA2DError(RuntimeError):
+    def __init__(self, status: int, detail: str = ""):
+        msg = "na2d status %d: %s" % (status, na2d_strerror(status))
+        if detail:
+            msg += " (%s)" % detail
+        super().__init__(msg)
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libna2d.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError("libna2d.so not built: run `python -c 'import __graft_entry__ as g; "
+                              "g.build()'` or `python vision_sliding_window_amd/_build.py`")
+        lib = ctypes.CDLL(LIBRARY)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        lib.na2d_forward.argtypes = [P, P, P, P, P] + [I] * 7 + [P]
+        lib.na2d_forward.restype = I
+        lib.na2d_forward_ex.argtypes = [P, P, P, P, P] + [I] * 8 + [P]
+        lib.na2d_forward_ex.restype = I
+        lib.na2d_check_args.argtypes = [P, P, P, P, P] + [I] * 8
+        lib.na2d_check_args.restype = I
+        lib.na2d_select_algo.argtypes = [I] * 5
+        lib.na2d_select_algo.restype = I
+        lib.na2d_strerror.argtypes = [I]
+        lib.na2d_strerror.restype = ctypes.c_char_p
+        lib.na2d_last_error.argtypes = []
+        lib.na2d_last_error.restype = ctypes.c_char_p
+        lib.na2d_version.argtypes = []
+        lib.na2d_version.restype = I
+        _lib = lib
+    return _lib
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, torch.cuda.Stream):
+        return s.cuda_stream
+    return int(s)
+
+
+def na2d_forward(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, stream=None) -> int:
+    return load().na2d_forward(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out),
+                               B, heads, H, W, d, ksize, dtype, _stream(stream))
+
+
+def na2d_forward_ex(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, algo,
+                    stream=None) -> int:
+    return load().na2d_forward_ex(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out),
+                                  B, heads, H, W, d, ksize, dtype, algo, _stream(stream))
+
+
+def na2d_check_args(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, algo) -> int:
+    return load().na2d_check_args(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out),
+                                  B, heads, H, W, d, ksize, dtype, algo)
+
+
+def na2d_select_algo(H, W, d, ksize, dtype) -> int:
+    return load().na2d_select_algo(H, W, d, ksize, dtype)
+
+
+def na2d_strerror(status: int) -> str:
+    return load().na2d_strerror(status).decode()
+
+
+def na2d_last_error() -> str:
+    return load().na2d_last_error().decode()
+
+
+def na2d_version() -> int:
+    return load().na2d_version()
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rpb, ksize: int,
+            algo: int = NA2D_ALGO_AUTO, out: torch.Tensor | None = None, stream=None):
+    """Fused NA2D forward on [B, heads, H, W, d] device tensors; returns fp32 out.
+
+    The tensors must be contiguous and on the GPU; ``stream`` defaults to
+    torch's current stream on q's device."""
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous() and t.dim() == 5):
+            raise ValueError("q, k, v must be contiguous 5-d GPU tensors [B, heads, H, W, d]")
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    if rpb is not None and not (rpb.is_cuda and rpb.is_contiguous() and rpb.dtype == torch.float32):
+        raise ValueError("rpb must be a contiguous float32 GPU tensor [heads, 2k-1, 2k-1]")
+    B, heads, H, W, d = q.shape
+    if rpb is not None and tuple(rpb.shape) != (heads, 2 * ksize - 1, 2 * ksize - 1):
+        raise ValueError("rpb must have shape [heads, 2k-1, 2k-1]")
+    if q.dtype not in TORCH_DTYPE_CODE:
+        raise ValueError("unsupported dtype %s" % q.dtype)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = na2d_forward_ex(q, k, v, rpb, out, B, heads, H, W, d, ksize, TORCH_DTYPE_CODE[q.dtype],
+                         algo, stream)
+    if st != NA2D_OK:
+        raise NA2DError(st, na2d_last_error() if st == NA2D_ERR_HIP else "")
+    return out
