@@ -113,7 +113,12 @@ def main():
     ap.add_argument("--algo", default="auto", choices=sorted(ALGOS))
     ap.add_argument("--min-footprint-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hot", action="store_true",
+                    help="also time one cache-resident input set (reported separately)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run a plain device-to-device copy of MIB "
+                         "MiB a few times (calibrates HBM byte counters under rocprofv3)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -122,6 +127,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": max(args.steps, 1)}), flush=True)
+        return
     from vision_sliding_window_amd import na2d
     from vision_sliding_window_amd.inputs import BENCH_WORKLOAD, WORKLOADS, workload_inputs
 
@@ -168,16 +182,16 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    # hot-cache figure (one set, L2/MALL resident), labelled as such
-    q, k, v, out = sets[0]
-    hs = torch.cuda.Event(enable_timing=True)
-    he = torch.cuda.Event(enable_timing=True)
-    hs.record(stream)
-    for _ in range(args.steps):
-        launch(0)
-    he.record(stream)
-    torch.cuda.synchronize()
-    hot_ms = hs.elapsed_time(he) / args.steps
+    hot_ms = None
+    if args.hot:  # cache-resident figure (one set, L2/MALL hits), labelled as such
+        hs = torch.cuda.Event(enable_timing=True)
+        he = torch.cuda.Event(enable_timing=True)
+        hs.record(stream)
+        for _ in range(args.steps):
+            launch(0)
+        he.record(stream)
+        torch.cuda.synchronize()
+        hot_ms = hs.elapsed_time(he) / args.steps
 
     value = w.queries / (ms * 1e-3)
     gbs = set_bytes / (ms * 1e-3) / 1e9
@@ -202,7 +216,7 @@ def main():
         "config": {"workload": wname, "B": w.B, "heads": w.heads, "H": w.H, "W": w.W, "d": w.d,
                    "k": w.k, "kernel": algo_name, "rotating_sets": nsets,
                    "footprint_bytes": nsets * set_bytes, "algorithmic_bytes_per_step": set_bytes,
-                   "hot_ms_per_step": round(hot_ms, 6),
+                   "hot_ms_per_step": None if hot_ms is None else round(hot_ms, 6),
                    "useful_tflops": round(tflops, 2)},
         "roofline": roofline,
     }

@@ -22,6 +22,7 @@ SOURCES = ["na2d_api.cpp", "na2d_valu.hip", "na2d_mfma.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function",
          "-I", INCLUDE, "-I", CSRC]
 

@@ -28,9 +28,10 @@ bool valu_supports(int d, int ksize) {
     return (d == 16 || d == 32 || d == 64 || d == 128) && ksize <= NA2D_VALU_MAX_KSIZE;
 }
 
-bool mfma_supports(int d, int ksize, int dtype) {
+// The MFMA kernel addresses one (b, h) map with 32-bit byte offsets.
+bool mfma_supports(int H, int W, int d, int ksize, int dtype) {
     return (dtype == NA2D_F16 || dtype == NA2D_BF16) && d == 32 && ksize >= 3 &&
-           ksize <= NA2D_MFMA_MAX_KSIZE;
+           ksize <= NA2D_MFMA_MAX_KSIZE && (uint64_t)H * W * d * 4 <= 0x7fffffffull;
 }
 
 // Size checks shared by every entry point.
@@ -46,10 +47,10 @@ int check_sizes(int B, int heads, int H, int W, int d, int ksize)
     return NA2D_OK;
 }
 
-int resolve_algo(int d, int ksize, int dtype, int algo)
+int resolve_algo(int H, int W, int d, int ksize, int dtype, int algo)
 {
     if (algo == NA2D_ALGO_AUTO)
-        return mfma_supports(d, ksize, dtype) ? NA2D_ALGO_MFMA : NA2D_ALGO_VALU;
+        return mfma_supports(H, W, d, ksize, dtype) ? NA2D_ALGO_MFMA : NA2D_ALGO_VALU;
     return algo;
 }
 
@@ -74,9 +75,9 @@ extern "C" int na2d_check_args(const void *q, const void *k, const void *v, cons
     if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
         overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, rpb, rpb_bytes))
         return NA2D_ERR_ALIAS;
-    const int a = resolve_algo(d, ksize, dtype, algo);
+    const int a = resolve_algo(H, W, d, ksize, dtype, algo);
     if (a == NA2D_ALGO_VALU && !valu_supports(d, ksize)) return NA2D_ERR_UNSUPPORTED;
-    if (a == NA2D_ALGO_MFMA && !mfma_supports(d, ksize, dtype)) return NA2D_ERR_UNSUPPORTED;
+    if (a == NA2D_ALGO_MFMA && !mfma_supports(H, W, d, ksize, dtype)) return NA2D_ERR_UNSUPPORTED;
     return NA2D_OK;
 }
 
@@ -85,7 +86,7 @@ extern "C" int na2d_select_algo(int H, int W, int d, int ksize, int dtype)
     if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
     int st = check_sizes(1, 1, H, W, d, ksize);
     if (st != NA2D_OK) return st;
-    const int a = resolve_algo(d, ksize, dtype, NA2D_ALGO_AUTO);
+    const int a = resolve_algo(H, W, d, ksize, dtype, NA2D_ALGO_AUTO);
     if (a == NA2D_ALGO_VALU && !valu_supports(d, ksize)) return NA2D_ERR_UNSUPPORTED;
     return a;
 }
@@ -98,7 +99,7 @@ extern "C" int na2d_forward_ex(const void *q, const void *k, const void *v, cons
     if (st != NA2D_OK) return st;
     const na2d::Problem p{q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype};
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = resolve_algo(d, ksize, dtype, algo) == NA2D_ALGO_MFMA
+    const hipError_t e = resolve_algo(H, W, d, ksize, dtype, algo) == NA2D_ALGO_MFMA
                              ? na2d::launch_mfma(p, s)
                              : na2d::launch_valu(p, s);
     if (e != hipSuccess) {

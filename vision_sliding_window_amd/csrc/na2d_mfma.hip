@@ -5,31 +5,38 @@
 // clamped ksize x ksize window, logits (q.k + B) / sqrt(d), softmax over the
 // window, weighted sum of the values.
 //
-// How (one workgroup = 4 waves = a TY x TX query tile, TY = 4 * QY, TX = QX):
-//  1. The tile's key/value halo -- the union of its queries' windows, at most
-//     (TY + ksize - 1) rows by 16 * NCB columns -- is copied once from HBM to
-//     LDS with 16-byte loads: K as [row][col][d] (16-byte d-slices swizzled
-//     against bank conflicts), V transposed as [d][row][col], plus this head's
-//     bias table scaled by log2(e)/sqrt(d) with a row and a column of -inf
-//     appended (used for keys outside a query's window).  This is the tiled
-//     design of the paperlayer summary's appendix A.4 (a query tile plus a key
-//     tile of side tq + k - 1 in on-chip memory), re-shaped for 64-lane waves.
-//  2. Each wave owns a QY x QX = 16-query subtile.  Its candidate keys are NR
-//     halo rows by 16 * NCB columns, cut into blocks of 16 keys (one row, 16
-//     consecutive columns).  For a block, S^T = K_block Q^T is one
-//     v_mfma_f32_16x16x32 (d = 32 is the contraction); in the result each lane
-//     holds one query (lane % 16) and four consecutive keys (4 * (lane / 16)
-//     + j).  Keys outside the query's own window get the -inf bias, so the
-//     result is exactly the masked window.
-//  3. Softmax is single-pass over chunks of RPC block rows: chunk max across
-//     the 4 lanes holding a query (two xor-shuffles), running max / sum with
-//     rescale, p = exp2(s - m).
+// How.  Persistent workgroups of 4 waves walk a list of query tiles of
+// TY x TX = (4 QY) x QX queries; each wave owns one QY x QX = 16-query subtile.
+//  1. Staging.  The tile's key/value halo -- the union of its queries'
+//     windows, at most TY + ksize - 1 rows by NC = 16 NCB columns -- is copied
+//     HBM -> LDS with buffer_load_dwordx4 ... lds (each lane's 16 bytes land
+//     at M0 + 16 lane; no VGPRs), as [row][col][d] for both K and V.  The
+//     16-byte d-slice s of pixel column c sits at slot s ^ ((c >> 2) & 3) so
+//     the reads below are free of bank conflicts.  Pixels outside the map get
+//     an out-of-range buffer offset and so arrive as zeros.  The queries go
+//     straight to registers.  This is the tiled design of the paperlayer
+//     summary's appendix A.4 (a query tile plus a key tile of side tq + k - 1
+//     in on-chip memory), re-shaped for 64-lane waves and LDS DMA.
+//  2. Logits.  The wave's candidate keys are NR halo rows by NC columns, in
+//     blocks of 16 (one row, 16 consecutive columns).  For a block,
+//     S^T = K_block Q^T is one v_mfma_f32_16x16x32 (d = 32 is the
+//     contraction); each lane then holds one query (lane % 16) and four
+//     consecutive keys (4 (lane / 16) + j).  The scaled bias is added from an
+//     LDS table holding -inf for keys outside the query's window, so the
+//     masked window is exact.
+//  3. Softmax, single pass over chunks of RPC block rows: the chunk max over
+//     the 4 lanes of a query (v_permlane16/32_swap, no LDS), running max and
+//     sum with rescale, p = exp2(s - m) with log2(e) folded into the scale.
 //  4. O^T = V^T P^T, again v_mfma_f32_16x16x32: the S^T layout above is
-//     exactly the B-operand layout of P^T for 32 keys (two blocks), and V^T
-//     comes from the transposed LDS copy with one 8-byte read per block.  P
-//     is fp16 for fp16 inputs; for bf16 inputs it is split into bf16 hi + lo
-//     parts (two products) so the weights keep ~16 bits.
-//  5. out = O / sum, written as fp32 with 16-byte stores.
+//     exactly the B-operand layout of P^T for 32 keys (two blocks), and
+//     ds_read_b64_tr_b16 hands each lane the 4 keys' values of its d from the
+//     [row][col][d] copy of V.  P is fp16 for fp16 inputs; for bf16 inputs it
+//     is split into bf16 hi + lo parts (two products), so the weights keep
+//     ~16 bits either way.
+//  5. out = O / sum in fp32 with 16-byte buffer stores (out-of-map lanes get
+//     an out-of-range offset and are dropped).
+// Pipelining: the next tile's copies are issued before this tile's stores,
+// and the wait for them (vmcnt(2)) leaves the two stores in flight.
 // No ksize^2-wide tensor ever leaves the chip.
 #include "na2d.h"
 #include "na2d_launch.h"
@@ -42,12 +49,24 @@ namespace na2d {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const unsigned char lds_cu8;
+typedef __attribute__((address_space(3))) const u32x4 lds_cu4;
+typedef __attribute__((address_space(3))) const float lds_cf32;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int kD = 32;        // head dim handled here
 constexpr int kWaves = 4;     // waves per workgroup, stacked vertically
 constexpr int kThreads = 64 * kWaves;
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+constexpr unsigned kOutOfRange = 0x7ffffff0u;  // byte offset past any map: loads 0, stores dropped
 
 template <typename T> struct Frag;
 template <> struct Frag<_Float16> { typedef half8 type; };
@@ -62,6 +81,34 @@ __device__ inline floatx4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Max and sum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 that hold one query.
+// v_permlane16_swap(x, x) returns both members of each (l, l ^ 16) pair in its
+// two results (and likewise permlane32 for l ^ 32), so op(r0, r1) is the
+// pairwise reduction -- the same value, bit for bit, in both lanes.
+__device__ inline float quad_max(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float quad_sum(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Hide a pointer's provenance from the optimiser (an empty asm that "may
+// change" the register), so it is not re-derived from a shared base plus a
+// large per-access constant.
+template <typename P>
+__device__ inline void opaque(P *&p)
+{
+    asm volatile("" : "+v"(p));
+}
+
 // Start of the window of ks pixels around i on an axis of length L.
 __device__ inline int window_start(int i, int ks, int L)
 {
@@ -74,11 +121,11 @@ struct Args {
     const void *q, *k, *v;
     const float *rpb;
     float *out;
-    int heads, H, W, ks;
+    int B, heads, H, W, ks;
     int tiles_x, tiles_y;  // tiles per map
-    unsigned ntiles;       // maps * tiles_y * tiles_x
+    unsigned ntiles;       // heads * B * tiles_y * tiles_x
     int lr;                // halo rows held in LDS
-    int ds;                // LDS stride (in elements) between two d-rows of V^T
+    int xcd_split;         // 1: tiles split into 8 contiguous ranges, one per XCD
     float c;               // log2(e) / sqrt(d)
 };
 
@@ -88,6 +135,7 @@ struct Shape {
     static constexpr int TX = QX;                   // tile cols
     static constexpr int NC = 16 * NCB;             // halo cols held in LDS
     static constexpr int BPC = RPC * NCB;           // key blocks per chunk
+    static constexpr int P = NC + QX - 1;           // interior bias table pitch
     static_assert(QY * QX == 16, "a wave owns 16 queries");
     static_assert(BPC % 2 == 0, "P.V consumes key blocks in pairs");
 };
@@ -99,154 +147,231 @@ __host__ __device__ inline int wave_rows(int QY, int RPC, int ks)
     return (n + RPC - 1) / RPC * RPC;
 }
 
+// LDS layout: K and V halos as [lr][NC pixels][4 x 16-byte d-slices], the
+// head's general bias table [2k][2k] floats, the interior table
+// [NR + QY - 1][NC + QX - 1] floats (see stage_bias).
+__host__ __device__ inline unsigned halo_bytes(int lr, int nc) { return (unsigned)lr * nc * 64u; }
+__host__ __device__ inline unsigned b_offset(int lr, int nc) { return 2u * halo_bytes(lr, nc); }
+__host__ __device__ inline unsigned bi_offset(int lr, int nc, int ks)
+{
+    return b_offset(lr, nc) + (unsigned)(4 * ks * ks) * 4u;
+}
+__host__ __device__ inline unsigned lds_bytes(int lr, int nc, int ks, int nr, int qy, int p)
+{
+    return (bi_offset(lr, nc, ks) + (unsigned)((nr + qy - 1) * p) * 4u + 15u) & ~15u;
+}
+
+// Where one query tile sits (uniform across the workgroup).
+struct Tile {
+    int h, y0, x0, hy0, hr, cx;
+    int64_t map_base;  // first pixel of the (b, h) map
+};
+
+template <int TY, int TX, int NC>
+__device__ inline Tile tile_geometry(const Args &a, unsigned t)
+{
+    // tiles are numbered head-major (head, batch, tile row, tile col), so that a
+    // run of consecutive tiles shares one head and one bias table
+    const unsigned tpm = (unsigned)a.tiles_x * a.tiles_y;
+    const unsigned per_head = tpm * (unsigned)a.B;
+    Tile g;
+    g.h = (int)(t / per_head);
+    const unsigned rem = t - (unsigned)g.h * per_head;
+    const unsigned b = rem / tpm, tr = rem - b * tpm;
+    const int ty = (int)(tr / a.tiles_x), tx = (int)(tr - (unsigned)ty * a.tiles_x);
+    g.map_base = ((int64_t)b * a.heads + g.h) * a.H * a.W;
+    g.y0 = ty * TY;
+    g.x0 = tx * TX;
+    // halo rows [hy0, hy0 + hr) hold every window of the tile's rows; LDS has
+    // lr >= hr rows, the ones past the map zero-filled
+    g.hr = min(TY + a.ks - 1, a.H);
+    g.hy0 = min(window_start(g.y0, a.ks, a.H), a.H - g.hr);
+    // halo cols [cx, cx + NC) hold the windows of columns x0 .. x0 + TX - 1
+    g.cx = a.W >= NC ? min(window_start(g.x0, a.ks, a.W), a.W - NC) : 0;
+    return g;
+}
+
+// A raw buffer resource over one (b, h) map of a [B, heads, H, W, ...] tensor.
+__device__ inline __amdgpu_buffer_rsrc_t map_rsrc(const void *base, int64_t map_base,
+                                                  unsigned pixel_bytes, unsigned map_bytes)
+{
+    const char *p = static_cast<const char *>(base) + map_base * pixel_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, (int)map_bytes,
+                                             (int)kRsrcWord3);
+}
+
+// This head's bias tables, times c = log2(e)/sqrt(d):
+//  - general [2k][2k]: the (2k-1)^2 table plus a row and a column of -inf
+//    (index 2k-1), used for key rows / columns outside a query's window;
+//  - interior [NR + QY - 1][P]: for a subtile none of whose queries is
+//    clamped, lane (qy, qx, g) reads element (row i, col c) of its candidate
+//    keys at (QY-1-qy+i) * P + (QX-1-qx+c); the entry holds the bias of that
+//    offset, or -inf where |dy| or |dx| exceeds k/2 (outside the window).
+// Every value of a pass is fetched before any is written.
+template <int QY, int QX, int NC>
+__device__ inline void stage_bias(const Args &a, int h, float *b_gen, float *b_int, int nr, int tid)
+{
+    constexpr int P = NC + QX - 1;
+    constexpr int MAXV = 8;  // per-thread values per pass
+    const int ks = a.ks, nb = 2 * ks - 1, tw = 2 * ks, r = ks >> 1;
+    const float *rb = a.rpb ? a.rpb + (int64_t)h * nb * nb : nullptr;
+    const int n_gen = tw * tw, n_int = (nr + QY - 1) * P, n = n_gen + n_int;
+    for (int base = 0; base < n; base += MAXV * kThreads) {
+        float val[MAXV];
+#pragma unroll
+        for (int e = 0; e < MAXV; ++e) {
+            const int u = base + e * kThreads + tid;
+            int br = -1, bc = -1;
+            if (u < n_gen) {
+                br = u / tw;
+                bc = u - br * tw;
+                if (br >= nb || bc >= nb) br = -1;
+            } else if (u < n) {
+                const int ui = u - n_gen, ai = ui / P, bi = ui - ai * P;
+                br = ai + r - (QY - 1);
+                bc = bi + r - (QX - 1);
+                if (br < ks - 1 - r || br > ks - 1 + r || bc < ks - 1 - r || bc > ks - 1 + r) br = -1;
+            }
+            val[e] = br < 0 ? -__builtin_inff() : (rb ? rb[br * nb + bc] * a.c : 0.f);
+        }
+#pragma unroll
+        for (int e = 0; e < MAXV; ++e) {
+            const int u = base + e * kThreads + tid;
+            if (u < n_gen) b_gen[u] = val[e];
+            else if (u < n) b_int[u - n_gen] = val[e];
+        }
+    }
+}
+
+// Issue the copies of one tile's K/V halo into LDS (each wave its rows) and
+// the load of this wave's queries into registers.
 template <typename T, int QY, int QX, int NCB, int RPC>
-__global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
+__device__ inline void stage_tile(const Args &a, const Tile &t, unsigned char *smem, int lr,
+                                  int wave, int lane, typename Frag<T>::type &qf)
+{
+    using S = Shape<QY, QX, NCB, RPC>;
+    const unsigned map_bytes = (unsigned)a.H * a.W * (kD * 2);
+    const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, t.map_base, kD * 2, map_bytes);
+    const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, t.map_base, kD * 2, map_bytes);
+    const int c_lane = lane >> 2;  // pixel column within a 16-column block
+    const int slot = lane & 3;
+    for (int r = wave; r < lr; r += kWaves) {
+        const int gy = t.hy0 + r;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int c = 16 * cb + c_lane;
+            const int sl = slot ^ ((c >> 2) & 3);  // the d-slice this LDS slot holds
+            const int gx = t.cx + c;
+            const unsigned off = gy < a.H && gx < a.W ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
+                                                      : kOutOfRange;
+            unsigned char *dk = smem + (unsigned)(r * S::NC + 16 * cb) * 64u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)dk, 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dk + halo_bytes(lr, S::NC)), 16,
+                                                     off, 0, 0, 0);
+        }
+    }
+    // queries: lane (g, qi) takes d-slice g of query qi (the B operand of S^T)
+    const int g = lane >> 4, qi = lane & 15;
+    const int y = min(t.y0 + QY * wave + qi / QX, a.H - 1);
+    const int x = min(t.x0 + qi % QX, a.W - 1);
+    const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, t.map_base, kD * 2, map_bytes);
+    const u32x4 qv =
+        __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0, 0);
+    qf = __builtin_bit_cast(typename Frag<T>::type, qv);
+}
+
+// Attention for one wave's 16 queries of tile t, reading the staged halo.
+// Leaves the unnormalised output in o (lane: query lane % 16, d = 16 dh +
+// 4 (lane / 16) + j) and the softmax sum of this lane's keys in lsum.
+// `ry` is the wave's first candidate key row (map coordinates).
+// INTERIOR: no query of the subtile is clamped and the candidate keys start
+// k/2 rows above / columns left of the first query, so bias and window mask
+// come from the interior table at a per-lane base plus fixed offsets.
+template <typename T, int QY, int QX, int NCB, int RPC, bool INTERIOR>
+__device__ inline void attend(const Args &a, const Tile &t, const unsigned char *smem, int lr,
+                              int wave, int ry, int lane, const typename Frag<T>::type &qf,
+                              floatx4 (&o)[2], float &lsum)
 {
     using S = Shape<QY, QX, NCB, RPC>;
     using FragT = typename Frag<T>::type;
-    extern __shared__ __align__(16) unsigned char smem[];
-
+    constexpr int P = S::P;
     const int ks = a.ks, H = a.H, W = a.W;
-    const int lr = a.lr, ds = a.ds;
     const int nr = wave_rows(QY, RPC, ks);
-    const int tw = 2 * ks;  // bias table row width (2k-1 entries + one -inf column)
-
-    uint4 *ks_lds = reinterpret_cast<uint4 *>(smem);                          // [lr][NC][4]
-    T *vt_lds = reinterpret_cast<T *>(smem + (size_t)lr * S::NC * kD * sizeof(T));  // [kD][ds]
-    float *b_lds = reinterpret_cast<float *>(smem + (size_t)lr * S::NC * kD * sizeof(T) +
-                                             (size_t)kD * ds * sizeof(T));    // [tw][tw]
-
-    // ---- which tile: consecutive tiles of a map go to the same XCD (the 8
-    // XCDs receive workgroups round-robin and each has its own L2, which then
-    // serves the halo overlap between neighbouring tiles).
-    unsigned tile;
-    {
-        const unsigned n = a.ntiles, bid = blockIdx.x;
-        const unsigned xcd = bid & 7u, slot = bid >> 3;
-        const unsigned per = n >> 3, rem = n & 7u;
-        tile = xcd * per + (xcd < rem ? xcd : rem) + slot;
-    }
-    const unsigned tiles_per_map = (unsigned)a.tiles_x * a.tiles_y;
-    const unsigned map = tile / tiles_per_map;
-    const unsigned tr = tile - map * tiles_per_map;
-    const int ty = (int)(tr / a.tiles_x), tx = (int)(tr % a.tiles_x);
-    const int h = (int)(map % (unsigned)a.heads);
-    const int64_t map_base = (int64_t)map * H * W;  // first pixel of this (b, h) map
-
-    const int y0 = ty * S::TY, x0 = tx * S::TX;
-    // halo rows [hy0, hy0 + lr): every window of the tile's rows lies in
-    // [hy0, hy0 + min(TY + ks - 1, H)); rows at or beyond H are zero-filled.
-    const int hr = min(S::TY + ks - 1, H);
-    const int hy0 = min(window_start(y0, ks, H), H - hr);
-    // halo cols [cx, cx + NC): covers the windows of columns x0 .. x0 + QX - 1
-    const int cx = W >= S::NC ? min(window_start(x0, ks, W), W - S::NC) : 0;
-
-    const int tid = threadIdx.x;
-    // ---- stage K: 16-byte d-slices, slot swizzled by column
-    {
-        const uint4 *kg = reinterpret_cast<const uint4 *>(a.k);
-        const int units = lr * S::NC * 4;
-        for (int u = tid; u < units; u += kThreads) {
-            const int r = u / (S::NC * 4), rem = u - r * (S::NC * 4);
-            const int j = rem >> 2, s = rem & 3;
-            const int gy = hy0 + r, gx = cx + j;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (gy < H && gx < W) val = kg[((map_base + (int64_t)gy * W + gx) * kD) / 8 + s];
-            ks_lds[(r * S::NC + j) * 4 + (s ^ ((j >> 2) & 3))] = val;
-        }
-    }
-    // ---- stage V transposed: a thread takes one d-slice of 4 consecutive columns
-    {
-        const uint4 *vg = reinterpret_cast<const uint4 *>(a.v);
-        const int units = lr * S::NC;  // lr rows * NC/4 column groups * 4 slices
-        for (int u = tid; u < units; u += kThreads) {
-            const int r = u / S::NC, rem = u - r * S::NC;
-            const int jg = rem >> 2, s = rem & 3;
-            const int gy = hy0 + r;
-            uint4 px[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int gx = cx + 4 * jg + i;
-                px[i] = make_uint4(0, 0, 0, 0);
-                if (gy < H && gx < W) px[i] = vg[((map_base + (int64_t)gy * W + gx) * kD) / 8 + s];
-            }
-            const unsigned short *e0 = reinterpret_cast<const unsigned short *>(&px[0]);
-            const unsigned short *e1 = reinterpret_cast<const unsigned short *>(&px[1]);
-            const unsigned short *e2 = reinterpret_cast<const unsigned short *>(&px[2]);
-            const unsigned short *e3 = reinterpret_cast<const unsigned short *>(&px[3]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint2 w;
-                w.x = (unsigned)e0[e] | ((unsigned)e1[e] << 16);
-                w.y = (unsigned)e2[e] | ((unsigned)e3[e] << 16);
-                *reinterpret_cast<uint2 *>(vt_lds + (size_t)(8 * s + e) * ds + r * S::NC + 4 * jg) = w;
-            }
-        }
-    }
-    // ---- bias table of this head, times c; last row and last column -inf
-    {
-        const int nb = 2 * ks - 1;
-        const float *rb = a.rpb ? a.rpb + (int64_t)h * nb * nb : nullptr;
-        for (int u = tid; u < tw * tw; u += kThreads) {
-            const int r = u / tw, cc = u - r * tw;
-            float val = -__builtin_inff();
-            if (r < nb && cc < nb) val = rb ? rb[r * nb + cc] * a.c : 0.f;
-            b_lds[u] = val;
-        }
-    }
-    __syncthreads();
-
-    // ---- per-wave work
-    const int lane = tid & 63, w = tid >> 6;
+    const int tw = 2 * ks;
     const int g = lane >> 4, qi = lane & 15;
-    int y = y0 + QY * w + qi / QX;
-    int x = x0 + qi % QX;
-    const bool store_ok = y < H && x < W;
-    y = min(y, H - 1);
-    x = min(x, W - 1);
-    const int sy = window_start(y, ks, H), sx = window_start(x, ks, W);
-    const int y1 = min(y0 + QY * w, H - 1);
-    const int ry = max(hy0, min(window_start(y1, ks, H), hy0 + hr - nr));  // wave's first key row
-    const int rrel = ry - hy0;
-    const int64_t qoff = map_base + (int64_t)y * W + x;
+    const int qy = qi / QX, qx = qi % QX;
+    const int y = min(t.y0 + QY * wave + qy, H - 1);
+    const int x = min(t.x0 + qx, W - 1);
+    const int rrel = ry - t.hy0;
 
-    const FragT qf = *reinterpret_cast<const FragT *>(static_cast<const T *>(a.q) + qoff * kD + 8 * g);
+    // K block row: 16 lanes read 16 columns' d-slice g (swizzled slot)
+    lds_cu8 *kp = (lds_cu8 *)(smem + (unsigned)(rrel * S::NC) * 64u + (unsigned)qi * 64u +
+                              16u * (unsigned)(g ^ ((qi >> 2) & 3)));
+    // V^T fragment via the transposing read: lane (g, qi) supplies dims
+    // 16 dh + 4 (qi & 3) .. + 3 of column 4 g + (qi >> 2) and receives dim
+    // 16 dh + qi of columns 4 g .. 4 g + 3
+    const unsigned char *vbase = smem + halo_bytes(lr, S::NC) + (unsigned)(rrel * S::NC) * 64u +
+                                 (unsigned)(4 * g + (qi >> 2)) * 64u + 8u * (unsigned)(qi & 1);
+    lds_cu8 *vp0 = (lds_cu8 *)(vbase + 16u * (unsigned)((0 + ((qi >> 1) & 1)) ^ g));
+    lds_cu8 *vp1 = (lds_cu8 *)(vbase + 16u * (unsigned)((2 + ((qi >> 1) & 1)) ^ g));
 
-    // bias column (per lane, per held key column) or the -inf column when the
-    // key column is outside this query's window
-    int coloff[NCB][4];
+    // bias: interior -> per-lane base in the interior table; general -> the
+    // general table with per-row and per-column indices (the -inf row / column
+    // for keys outside the window)
+    lds_cf32 *bp;
+    int sy = 0, coloff[NCB][4];
+    if constexpr (INTERIOR) {
+        bp = (lds_cf32 *)(smem + bi_offset(lr, S::NC, ks)) + (QY - 1 - qy) * P + (QX - 1 - qx + 4 * g);
+    } else {
+        bp = (lds_cf32 *)(smem + b_offset(lr, S::NC));
+        sy = window_start(y, ks, H);
+        const int sx = window_start(x, ks, W);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = cx + 16 * cb + 4 * g + j;
-            coloff[cb][j] = (unsigned)(col - sx) < (unsigned)ks ? col - x + ks - 1 : 2 * ks - 1;
-        }
+            for (int j = 0; j < 4; ++j) {
+                const int col = t.cx + 16 * cb + 4 * g + j;
+                coloff[cb][j] = (unsigned)(col - sx) < (unsigned)ks ? col - x + ks - 1 : 2 * ks - 1;
+            }
+    }
+    // keep each per-lane LDS pointer in one register, so that every access
+    // below is that register plus an instruction offset
+    opaque(kp);
+    opaque(vp0);
+    opaque(vp1);
+    if constexpr (INTERIOR) opaque(bp);
 
-    float m = -__builtin_inff(), lsum = 0.f;
-    floatx4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    const int kslot = g ^ ((qi >> 2) & 3);  // swizzled d-slice this lane reads from K
+    float m = -__builtin_inff();
+    lsum = 0.f;
+    o[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+    o[1] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     for (int c0 = 0; c0 < nr; c0 += RPC) {
         float sc[RPC][NCB][4];
-        // logits S^T for this chunk's blocks
 #pragma unroll
         for (int rr = 0; rr < RPC; ++rr) {
-            const int i = c0 + rr;
-            const int krow = ry + i;
-            const int rowb = (unsigned)(krow - sy) < (unsigned)ks ? (krow - y + ks - 1) * tw
-                                                                   : (2 * ks - 1) * tw;
+            lds_cf32 *brow;
+            if constexpr (INTERIOR) {
+                brow = bp + rr * P;
+            } else {
+                const int krow = ry + c0 + rr;
+                brow = bp + ((unsigned)(krow - sy) < (unsigned)ks ? (krow - y + ks - 1) * tw
+                                                                   : (2 * ks - 1) * tw);
+            }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                const uint4 kv = ks_lds[((rrel + i) * S::NC + 16 * cb + qi) * 4 + kslot];
-                const FragT kf = *reinterpret_cast<const FragT *>(&kv);
+                const FragT kf =
+                    __builtin_bit_cast(FragT, *(lds_cu4 *)(kp + (rr * S::NC + 16 * cb) * 64));
                 const floatx4 acc = mfma16x16x32(kf, qf, floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    sc[rr][cb][j] = fmaf(acc[j], a.c, b_lds[rowb + coloff[cb][j]]);
+                for (int j = 0; j < 4; ++j) {
+                    float b;
+                    if constexpr (INTERIOR) b = brow[16 * cb + j];
+                    else b = brow[coloff[cb][j]];
+                    sc[rr][cb][j] = fmaf(acc[j], a.c, b);
+                }
             }
         }
-        // running max over the chunk and the 4 lanes that hold this query
         float mc = -__builtin_inff();
 #pragma unroll
         for (int rr = 0; rr < RPC; ++rr)
@@ -254,44 +379,47 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) mc = fmaxf(mc, sc[rr][cb][j]);
-        mc = fmaxf(mc, __shfl_xor(mc, 16));
-        mc = fmaxf(mc, __shfl_xor(mc, 32));
+        mc = quad_max(mc);
         const float mnew = fmaxf(m, mc);
         const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-        const float corr = __builtin_amdgcn_exp2f(m - muse);
+        if (c0 > 0) {  // rescale what earlier chunks accumulated
+            const float corr = __builtin_amdgcn_exp2f(m - muse);
+            lsum *= corr;
+#pragma unroll
+            for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[dh][j] *= corr;
+        }
         m = mnew;
-        lsum *= corr;
-#pragma unroll
-        for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[dh][j] *= corr;
 
-        // weights and P.V, two key blocks (32 keys) per product
 #pragma unroll
-        for (int bp = 0; bp < S::BPC; bp += 2) {
-            const int rA = bp / NCB, cbA = bp % NCB;
-            const int rB = (bp + 1) / NCB, cbB = (bp + 1) % NCB;
+        for (int bq = 0; bq < S::BPC; bq += 2) {
+            const int rA = bq / NCB, cbA = bq % NCB;
+            const int rB = (bq + 1) / NCB, cbB = (bq + 1) % NCB;
+            const int offA = (rA * S::NC + 16 * cbA) * 64, offB = (rB * S::NC + 16 * cbB) * 64;
+            FragT vf[2];
+#pragma unroll
+            for (int dh = 0; dh < 2; ++dh) {
+                lds_cu8 *vp = dh ? vp1 : vp0;
+                const v4i16 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vp + offA));
+                const v4i16 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vp + offB));
+                const v8i16 vv = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                vf[dh] = __builtin_bit_cast(FragT, vv);
+            }
             float p[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 p[j] = __builtin_amdgcn_exp2f(sc[rA][cbA][j] - muse);
                 p[4 + j] = __builtin_amdgcn_exp2f(sc[rB][cbB][j] - muse);
             }
-            FragT vf[2];
-#pragma unroll
-            for (int dh = 0; dh < 2; ++dh) {
-                const T *base = vt_lds + (size_t)(16 * dh + qi) * ds + 4 * g;
-                const uint2 va = *reinterpret_cast<const uint2 *>(base + (rrel + c0 + rA) * S::NC + 16 * cbA);
-                const uint2 vb = *reinterpret_cast<const uint2 *>(base + (rrel + c0 + rB) * S::NC + 16 * cbB);
-                uint4 vv = make_uint4(va.x, va.y, vb.x, vb.y);
-                vf[dh] = *reinterpret_cast<const FragT *>(&vv);
-            }
-            if constexpr (sizeof(T) == 2 && __is_same(T, _Float16)) {
+            if constexpr (__is_same(T, _Float16)) {
                 half8 pf;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) pf[j] = static_cast<_Float16>(p[j]);
+                // the sum takes the rounded weights, so they sum to exactly what multiplies V
 #pragma unroll
-                for (int j = 0; j < 8; ++j) lsum += static_cast<float>(pf[j]);
+                for (int j = 0; j < 8; j += 2)
+                    lsum = __builtin_amdgcn_fdot2(half2{pf[j], pf[j + 1]}, half2{1, 1}, lsum, false);
 #pragma unroll
                 for (int dh = 0; dh < 2; ++dh) o[dh] = mfma16x16x32(vf[dh], pf, o[dh]);
             } else {
@@ -309,17 +437,130 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
                 }
             }
         }
+        kp += RPC * S::NC * 64;
+        vp0 += RPC * S::NC * 64;
+        vp1 += RPC * S::NC * 64;
+        if constexpr (INTERIOR) bp += RPC * P;
     }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    if (store_ok) {
-        const float inv = 1.f / lsum;
-        float *dst = a.out + qoff * kD + 4 * g;
+}
+
+// One wave's share of a tile: choose its candidate key rows, take the
+// interior or the general path, leave o / lsum for store_out.
+template <typename T, int QY, int QX, int NCB, int RPC>
+__device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned char *smem, int lr,
+                                   int wave, int lane, const typename Frag<T>::type &qf,
+                                   floatx4 (&o)[2], float &lsum)
+{
+    const int ks = a.ks, H = a.H, W = a.W, r = ks >> 1;
+    const int nr = wave_rows(QY, RPC, ks);
+    const int y1 = t.y0 + QY * wave;
+    const int ry = max(t.hy0, min(window_start(min(y1, H - 1), ks, H), t.hy0 + t.hr - nr));
+    const bool interior = y1 - r >= 0 && y1 + QY - 1 + r <= H - 1 && t.x0 - r >= 0 &&
+                          t.x0 + QX - 1 + r <= W - 1 && ry == y1 - r && t.cx == t.x0 - r;
+    if (interior)
+        attend<T, QY, QX, NCB, RPC, true>(a, t, smem, lr, wave, ry, lane, qf, o, lsum);
+    else
+        attend<T, QY, QX, NCB, RPC, false>(a, t, smem, lr, wave, ry, lane, qf, o, lsum);
+}
+
+// Normalise and write one wave's 16 outputs: exactly two 16-byte buffer
+// stores per lane, out-of-map queries dropped by the range check.
+template <int QY, int QX>
+__device__ inline void store_out(const Args &a, const Tile &t, int wave, int lane,
+                                 const floatx4 (&o)[2], float lsum)
+{
+    const int g = lane >> 4, qi = lane & 15;
+    const float inv = __builtin_amdgcn_rcpf(quad_sum(lsum));
+    const int y = t.y0 + QY * wave + qi / QX;
+    const int x = t.x0 + qi % QX;
+    const unsigned off = y < a.H && x < a.W ? (unsigned)(y * a.W + x) * 128u + 16u * g : kOutOfRange;
+    const __amdgpu_buffer_rsrc_t ro =
+        map_rsrc(a.out, t.map_base, kD * 4, (unsigned)a.H * a.W * (kD * 4));
 #pragma unroll
-        for (int dh = 0; dh < 2; ++dh)
-            *reinterpret_cast<float4 *>(dst + 16 * dh) =
-                make_float4(o[dh][0] * inv, o[dh][1] * inv, o[dh][2] * inv, o[dh][3] * inv);
+    for (int dh = 0; dh < 2; ++dh) {
+        const floatx4 v = o[dh] * inv;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off + 64u * dh, 0, 0);
     }
+}
+
+// s_waitcnt on vmcnt alone (gfx9 encoding: expcnt and lgkmcnt left at their maxima).
+#define NA2D_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Persistent workgroups.  Workgroup w takes every G-th tile of its range (the
+// whole tile list, or with xcd_split its XCD's eighth of it, so the
+// workgroups sharing an L2 work on neighbouring tiles).  Per tile: attend,
+// barrier, issue the next tile's copies, store this tile's outputs, wait for
+// the copies only, barrier.
+template <typename T, int QY, int QX, int NCB, int RPC>
+__global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
+{
+    using S = Shape<QY, QX, NCB, RPC>;
+    using FragT = typename Frag<T>::type;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = a.lr;
+    const int nr = wave_rows(QY, RPC, a.ks);
+
+    unsigned tile, step, end;
+    if (a.xcd_split) {
+        const unsigned xcd = blockIdx.x & 7u;
+        tile = (unsigned)(((uint64_t)a.ntiles * xcd) >> 3) + (blockIdx.x >> 3);
+        end = (unsigned)(((uint64_t)a.ntiles * (xcd + 1)) >> 3);
+        step = gridDim.x >> 3;
+    } else {
+        tile = blockIdx.x;
+        end = a.ntiles;
+        step = gridDim.x;
+    }
+    if (tile >= end) return;
+
+    float *b_gen = reinterpret_cast<float *>(smem + b_offset(lr, S::NC));
+    float *b_int = reinterpret_cast<float *>(smem + bi_offset(lr, S::NC, a.ks));
+    FragT qf;
+    Tile t = tile_geometry<S::TY, S::TX, S::NC>(a, tile);
+    int bias_head = t.h;
+    stage_bias<QY, QX, S::NC>(a, t.h, b_gen, b_int, nr, tid);
+    stage_tile<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    while (true) {
+        floatx4 o[2];
+        float lsum;
+        attend_wave<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf, o, lsum);
+        const Tile done = t;
+        const unsigned next = tile + step;
+        __syncthreads();  // every wave is done reading the LDS copy
+        if (next < end) {
+            t = tile_geometry<S::TY, S::TX, S::NC>(a, next);
+            if (t.h != bias_head) {  // rare: the tile list is head-major
+                stage_bias<QY, QX, S::NC>(a, t.h, b_gen, b_int, nr, tid);
+                bias_head = t.h;
+            }
+            stage_tile<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf);
+        }
+        asm volatile("" ::: "memory");  // keep the stores after the copies just issued
+        store_out<QY, QX>(a, done, wave, lane, o, lsum);
+        if (next >= end) break;
+        NA2D_WAIT_VMCNT(2);  // the copies (older than the two stores) have landed
+        __syncthreads();
+        tile = next;
+    }
+}
+
+int device_cus()
+{
+    static thread_local int cached_dev = -1, cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
 }
 
 template <typename T, int QY, int QX, int NCB, int RPC>
@@ -332,6 +573,7 @@ hipError_t launch_cfg(const Problem &p, hipStream_t stream)
     a.v = p.v;
     a.rpb = p.rpb;
     a.out = p.out;
+    a.B = p.B;
     a.heads = p.heads;
     a.H = p.H;
     a.W = p.W;
@@ -343,21 +585,27 @@ hipError_t launch_cfg(const Problem &p, hipStream_t stream)
     a.ntiles = (unsigned)ntiles;
     const int nr = wave_rows(QY, RPC, p.ksize);
     a.lr = max(S::TY + p.ksize - 1, nr);
-    // V^T row stride in elements: lr * NC, padded so that the 16 d-rows read
-    // by one 16-lane group start in different LDS banks (stride = 2 mod 32 dwords)
-    int dsw = a.lr * S::NC / 2;
-    dsw += (2 - dsw % 32 + 32) % 32;
-    a.ds = 2 * dsw;
     a.c = 1.4426950408889634f / sqrtf((float)kD);
-    const size_t lds = (size_t)a.lr * S::NC * kD * sizeof(T) + (size_t)kD * a.ds * sizeof(T) +
-                       (size_t)(2 * p.ksize) * (2 * p.ksize) * sizeof(float);
+    const size_t lds = lds_bytes(a.lr, S::NC, p.ksize, nr, QY, S::P);
     auto kern = na2d_mfma_kernel<T, QY, QX, NCB, RPC>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(a.ntiles), dim3(kThreads), lds, stream, a);
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds);
+    if (e != hipSuccess) return e;
+    const int cus = device_cus();
+    if (per_cu <= 0 || cus <= 0) return hipErrorInvalidConfiguration;
+    uint64_t grid = (uint64_t)cus * per_cu;
+    if (grid > ntiles) grid = ntiles;
+    a.xcd_split = 0;
+    if (grid >= 64) {  // enough workgroups to give every XCD its own tile range
+        grid &= ~7ull;
+        a.xcd_split = 1;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -376,6 +624,8 @@ hipError_t launch_typed(const Problem &p, hipStream_t stream)
 hipError_t launch_mfma(const Problem &p, hipStream_t stream)
 {
     if (p.d != kD || p.ksize < 3 || p.ksize > NA2D_MFMA_MAX_KSIZE) return hipErrorInvalidValue;
+    // byte offsets inside one map are 32-bit (buffer addressing)
+    if ((uint64_t)p.H * p.W * (kD * 4) > 0x7fffffffull) return hipErrorInvalidValue;
     if (p.dtype == NA2D_F16) return launch_typed<_Float16>(p, stream);
     if (p.dtype == NA2D_BF16) return launch_typed<__bf16>(p, stream);
     return hipErrorInvalidValue;
