@@ -44,6 +44,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 
 namespace na2d {
 namespace {
@@ -136,29 +137,42 @@ struct Shape {
     static constexpr int NC = 16 * NCB;             // halo cols held in LDS
     static constexpr int BPC = RPC * NCB;           // key blocks per chunk
     static constexpr int P = NC + QX - 1;           // interior bias table pitch
+    static constexpr int PC = 2 * NC - 1;           // class table pitch
+    // class tables (one per column class, see stage_bias) for one 16-column
+    // block and k <= 9; otherwise a general table plus an interior table
+    static constexpr bool CLS = NCB == 1 && QX == 8;
     static_assert(QY * QX == 16, "a wave owns 16 queries");
     static_assert(BPC % 2 == 0, "P.V consumes key blocks in pairs");
 };
 
 // Rows of candidate keys per wave: QY + ks - 1 rounded up to whole chunks.
-__host__ __device__ inline int wave_rows(int QY, int RPC, int ks)
+__host__ __device__ constexpr int wave_rows(int QY, int RPC, int ks)
 {
     const int n = QY + ks - 1;
     return (n + RPC - 1) / RPC * RPC;
 }
 
-// LDS layout: K and V halos as [lr][NC pixels][4 x 16-byte d-slices], the
-// head's general bias table [2k][2k] floats, the interior table
-// [NR + QY - 1][NC + QX - 1] floats (see stage_bias).
+// LDS layout: K and V halos as [lr][NC pixels][4 x 16-byte d-slices], then
+// the head's bias tables (see stage_bias):
+//  - class layout: k tables [2k-1][PC] floats, then a -inf strip of
+//    RPC * PC + NC floats;
+//  - split layout: the general table [2k][2k], then the interior table
+//    [NR + QY - 1][P].
 __host__ __device__ inline unsigned halo_bytes(int lr, int nc) { return (unsigned)lr * nc * 64u; }
 __host__ __device__ inline unsigned b_offset(int lr, int nc) { return 2u * halo_bytes(lr, nc); }
 __host__ __device__ inline unsigned bi_offset(int lr, int nc, int ks)
 {
     return b_offset(lr, nc) + (unsigned)(4 * ks * ks) * 4u;
 }
-__host__ __device__ inline unsigned lds_bytes(int lr, int nc, int ks, int nr, int qy, int p)
+__host__ __device__ constexpr unsigned class_floats(int ks, int pc) { return (unsigned)ks * (2 * ks - 1) * pc; }
+__host__ __device__ constexpr unsigned bias_floats(bool cls, int ks, int nr, int qy, int qx, int nc, int rpc)
 {
-    return (bi_offset(lr, nc, ks) + (unsigned)((nr + qy - 1) * p) * 4u + 15u) & ~15u;
+    if (cls) return class_floats(ks, 2 * nc - 1) + (unsigned)(rpc * (2 * nc - 1) + nc);
+    return (unsigned)(4 * ks * ks) + (unsigned)((nr + qy - 1) * (nc + qx - 1));
+}
+__host__ __device__ inline unsigned lds_bytes(int lr, int nc, unsigned bfloats)
+{
+    return (b_offset(lr, nc) + bfloats * 4u + 15u) & ~15u;
 }
 
 // Where one query tile sits (uniform across the workgroup).
@@ -200,45 +214,68 @@ __device__ inline __amdgpu_buffer_rsrc_t map_rsrc(const void *base, int64_t map_
                                              (int)kRsrcWord3);
 }
 
-// This head's bias tables, times c = log2(e)/sqrt(d):
-//  - general [2k][2k]: the (2k-1)^2 table plus a row and a column of -inf
-//    (index 2k-1), used for key rows / columns outside a query's window;
-//  - interior [NR + QY - 1][P]: for a subtile none of whose queries is
-//    clamped, lane (qy, qx, g) reads element (row i, col c) of its candidate
-//    keys at (QY-1-qy+i) * P + (QX-1-qx+c); the entry holds the bias of that
-//    offset, or -inf where |dy| or |dx| exceeds k/2 (outside the window).
+// This head's bias tables, times c = log2(e)/sqrt(d), for keys inside a
+// query's window and -inf outside it.  Two layouts:
+//  - class (one 16-column block, k <= 9): a query's window columns depend on
+//    e_x = x - sx only (its offset inside the clamped window), so there is one
+//    table per e_x in [0, k): T_e[a][b'] = bias(a, b) for the relative offset
+//    (a, b) = (ky - y + k - 1, kx - x + k - 1), b = b' - (NC - k), when b lies
+//    in [k-1-e_x, 2k-2-e_x], else -inf.  A lane reads element (row i, col c)
+//    of its candidate keys at lane_base + i * PC + c; rows outside its window
+//    read from the -inf strip instead.
+//  - split: the general table [2k][2k] (the (2k-1)^2 table plus a -inf row
+//    and column at index 2k-1) and the interior table [NR + QY - 1][P]: for
+//    a subtile none of whose queries is clamped, lane (qy, qx, g) reads
+//    element (row i, col c) at (QY-1-qy+i) * P + (QX-1-qx+c), which holds the
+//    bias of that offset or -inf where |dy| or |dx| exceeds k/2.
 // Every value of a pass is fetched before any is written.
-template <int QY, int QX, int NC>
-__device__ inline void stage_bias(const Args &a, int h, float *b_gen, float *b_int, int nr, int tid)
+template <int QY, int QX, int NC, int RPC, bool CLS>
+__device__ inline void stage_bias(const Args &a, int ks, int h, float *bt, int nr, int tid)
 {
-    constexpr int P = NC + QX - 1;
+    constexpr int P = NC + QX - 1, PC = 2 * NC - 1;
     constexpr int MAXV = 8;  // per-thread values per pass
-    const int ks = a.ks, nb = 2 * ks - 1, tw = 2 * ks, r = ks >> 1;
+    const int nb = 2 * ks - 1, tw = 2 * ks, r = ks >> 1;
     const float *rb = a.rpb ? a.rpb + (int64_t)h * nb * nb : nullptr;
-    const int n_gen = tw * tw, n_int = (nr + QY - 1) * P, n = n_gen + n_int;
+    int n1, n;
+    if constexpr (CLS) {
+        n1 = (int)class_floats(ks, PC);
+        n = n1 + RPC * PC + NC;
+    } else {
+        n1 = tw * tw;
+        n = n1 + (nr + QY - 1) * P;
+    }
     for (int base = 0; base < n; base += MAXV * kThreads) {
         float val[MAXV];
 #pragma unroll
         for (int e = 0; e < MAXV; ++e) {
             const int u = base + e * kThreads + tid;
             int br = -1, bc = -1;
-            if (u < n_gen) {
-                br = u / tw;
-                bc = u - br * tw;
-                if (br >= nb || bc >= nb) br = -1;
-            } else if (u < n) {
-                const int ui = u - n_gen, ai = ui / P, bi = ui - ai * P;
-                br = ai + r - (QY - 1);
-                bc = bi + r - (QX - 1);
-                if (br < ks - 1 - r || br > ks - 1 + r || bc < ks - 1 - r || bc > ks - 1 + r) br = -1;
+            if constexpr (CLS) {
+                if (u < n1) {
+                    const int ex = u / (nb * PC), rem = u - ex * (nb * PC);
+                    br = rem / PC;
+                    bc = rem - br * PC - (NC - ks);
+                    if (bc < ks - 1 - ex || bc > 2 * ks - 2 - ex) br = -1;
+                }
+            } else {
+                if (u < n1) {
+                    br = u / tw;
+                    bc = u - br * tw;
+                    if (br >= nb || bc >= nb) br = -1;
+                } else if (u < n) {
+                    const int ui = u - n1, ai = ui / P, bi = ui - ai * P;
+                    br = ai + r - (QY - 1);
+                    bc = bi + r - (QX - 1);
+                    if (br < ks - 1 - r || br > ks - 1 + r || bc < ks - 1 - r || bc > ks - 1 + r)
+                        br = -1;
+                }
             }
             val[e] = br < 0 ? -__builtin_inff() : (rb ? rb[br * nb + bc] * a.c : 0.f);
         }
 #pragma unroll
         for (int e = 0; e < MAXV; ++e) {
             const int u = base + e * kThreads + tid;
-            if (u < n_gen) b_gen[u] = val[e];
-            else if (u < n) b_int[u - n_gen] = val[e];
+            if (u < n) bt[u] = val[e];
         }
     }
 }
@@ -283,19 +320,25 @@ __device__ inline void stage_tile(const Args &a, const Tile &t, unsigned char *s
 // Attention for one wave's 16 queries of tile t, reading the staged halo.
 // Leaves the unnormalised output in o (lane: query lane % 16, d = 16 dh +
 // 4 (lane / 16) + j) and the softmax sum of this lane's keys in lsum.
-// `ry` is the wave's first candidate key row (map coordinates).
-// INTERIOR: no query of the subtile is clamped and the candidate keys start
-// k/2 rows above / columns left of the first query, so bias and window mask
-// come from the interior table at a per-lane base plus fixed offsets.
-template <typename T, int QY, int QX, int NCB, int RPC, bool INTERIOR>
-__device__ inline void attend(const Args &a, const Tile &t, const unsigned char *smem, int lr,
-                              int wave, int ry, int lane, const typename Frag<T>::type &qf,
-                              floatx4 (&o)[2], float &lsum)
+// `ry` is the wave's first candidate key row (map coordinates).  MODE picks
+// how bias and window mask are read (see stage_bias):
+//  kClass:    class tables; per-lane base plus fixed offsets, rows outside the
+//             window redirected to the -inf strip;
+//  kInterior: split layout, no query of the subtile clamped, candidate keys
+//             start k/2 rows above / columns left of the first query;
+//  kGeneral:  split layout, general table with per-row / per-column indices.
+enum { kClass = 0, kInterior = 1, kGeneral = 2 };
+
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int MODE>
+__device__ inline void attend(const Args &a, const Tile &t, const unsigned char *smem,
+                              const float *btab, int lr, int wave, int ry, int lane,
+                              const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum)
 {
     using S = Shape<QY, QX, NCB, RPC>;
     using FragT = typename Frag<T>::type;
-    constexpr int P = S::P;
-    const int ks = a.ks, H = a.H, W = a.W;
+    constexpr int P = S::P, PC = S::PC;
+    const int ks = KS ? KS : a.ks;
+    const int H = a.H, W = a.W;
     const int nr = wave_rows(QY, RPC, ks);
     const int tw = 2 * ks;
     const int g = lane >> 4, qi = lane & 15;
@@ -315,15 +358,21 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
     lds_cu8 *vp0 = (lds_cu8 *)(vbase + 16u * (unsigned)((0 + ((qi >> 1) & 1)) ^ g));
     lds_cu8 *vp1 = (lds_cu8 *)(vbase + 16u * (unsigned)((2 + ((qi >> 1) & 1)) ^ g));
 
-    // bias: interior -> per-lane base in the interior table; general -> the
-    // general table with per-row and per-column indices (the -inf row / column
-    // for keys outside the window)
-    lds_cf32 *bp;
-    int sy = 0, coloff[NCB][4];
-    if constexpr (INTERIOR) {
-        bp = (lds_cf32 *)(smem + bi_offset(lr, S::NC, ks)) + (QY - 1 - qy) * P + (QX - 1 - qx + 4 * g);
+    lds_cf32 *bp;          // per-lane bias base (advanced per chunk)
+    lds_cf32 *bneg = nullptr;
+    int sy = 0, lo = 0, coloff[NCB][4];
+    if constexpr (MODE == kClass) {
+        sy = window_start(y, ks, H);
+        const int ex = x - window_start(x, ks, W);
+        lo = sy - ry;  // first candidate row inside the window
+        const int nb = 2 * ks - 1;
+        bp = (lds_cf32 *)btab + ex * (nb * PC) + (ry - y + ks - 1) * PC + (t.cx - x + ks - 1) +
+             (S::NC - ks) + 4 * g;
+        bneg = (lds_cf32 *)btab + class_floats(ks, PC) + 4 * g;
+    } else if constexpr (MODE == kInterior) {
+        bp = (lds_cf32 *)btab + 4 * ks * ks + (QY - 1 - qy) * P + (QX - 1 - qx + 4 * g);
     } else {
-        bp = (lds_cf32 *)(smem + b_offset(lr, S::NC));
+        bp = (lds_cf32 *)btab;
         sy = window_start(y, ks, H);
         const int sx = window_start(x, ks, W);
 #pragma unroll
@@ -339,7 +388,8 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
     opaque(kp);
     opaque(vp0);
     opaque(vp1);
-    if constexpr (INTERIOR) opaque(bp);
+    if constexpr (MODE != kGeneral) opaque(bp);
+    if constexpr (MODE == kClass) opaque(bneg);
 
     float m = -__builtin_inff();
     lsum = 0.f;
@@ -351,7 +401,12 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 #pragma unroll
         for (int rr = 0; rr < RPC; ++rr) {
             lds_cf32 *brow;
-            if constexpr (INTERIOR) {
+            if constexpr (MODE == kClass) {
+                // rows k .. nr-1-(nr-k) are inside every window when nr is fixed
+                const bool always = KS && RPC == wave_rows(QY, RPC, KS) &&
+                                    rr >= wave_rows(QY, RPC, KS) - KS && rr < KS;
+                brow = (always || (unsigned)(c0 + rr - lo) < (unsigned)ks ? bp : bneg) + rr * PC;
+            } else if constexpr (MODE == kInterior) {
                 brow = bp + rr * P;
             } else {
                 const int krow = ry + c0 + rr;
@@ -366,8 +421,8 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     float b;
-                    if constexpr (INTERIOR) b = brow[16 * cb + j];
-                    else b = brow[coloff[cb][j]];
+                    if constexpr (MODE == kGeneral) b = brow[coloff[cb][j]];
+                    else b = brow[16 * cb + j];
                     sc[rr][cb][j] = fmaf(acc[j], a.c, b);
                 }
             }
@@ -440,27 +495,38 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
         kp += RPC * S::NC * 64;
         vp0 += RPC * S::NC * 64;
         vp1 += RPC * S::NC * 64;
-        if constexpr (INTERIOR) bp += RPC * P;
+        if constexpr (MODE == kClass) {
+            bp += RPC * PC;  // the -inf strip is long enough for any chunk
+        } else if constexpr (MODE == kInterior) {
+            bp += RPC * P;
+        }
     }
 }
 
-// One wave's share of a tile: choose its candidate key rows, take the
-// interior or the general path, leave o / lsum for store_out.
-template <typename T, int QY, int QX, int NCB, int RPC>
-__device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned char *smem, int lr,
-                                   int wave, int lane, const typename Frag<T>::type &qf,
-                                   floatx4 (&o)[2], float &lsum)
+// One wave's share of a tile: choose its candidate key rows and the bias
+// path, leave o / lsum for store_out.
+template <typename T, int QY, int QX, int NCB, int RPC, int KS>
+__device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned char *smem,
+                                   const float *btab, int lr, int wave, int lane,
+                                   const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum)
 {
-    const int ks = a.ks, H = a.H, W = a.W, r = ks >> 1;
+    using S = Shape<QY, QX, NCB, RPC>;
+    const int ks = KS ? KS : a.ks, H = a.H, W = a.W, r = ks >> 1;
     const int nr = wave_rows(QY, RPC, ks);
     const int y1 = t.y0 + QY * wave;
     const int ry = max(t.hy0, min(window_start(min(y1, H - 1), ks, H), t.hy0 + t.hr - nr));
-    const bool interior = y1 - r >= 0 && y1 + QY - 1 + r <= H - 1 && t.x0 - r >= 0 &&
-                          t.x0 + QX - 1 + r <= W - 1 && ry == y1 - r && t.cx == t.x0 - r;
-    if (interior)
-        attend<T, QY, QX, NCB, RPC, true>(a, t, smem, lr, wave, ry, lane, qf, o, lsum);
-    else
-        attend<T, QY, QX, NCB, RPC, false>(a, t, smem, lr, wave, ry, lane, qf, o, lsum);
+    if constexpr (S::CLS) {
+        attend<T, QY, QX, NCB, RPC, KS, kClass>(a, t, smem, btab, lr, wave, ry, lane, qf, o, lsum);
+    } else {
+        const bool interior = y1 - r >= 0 && y1 + QY - 1 + r <= H - 1 && t.x0 - r >= 0 &&
+                              t.x0 + QX - 1 + r <= W - 1 && ry == y1 - r && t.cx == t.x0 - r;
+        if (interior)
+            attend<T, QY, QX, NCB, RPC, KS, kInterior>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
+                                                       lsum);
+        else
+            attend<T, QY, QX, NCB, RPC, KS, kGeneral>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
+                                                      lsum);
+    }
 }
 
 // Normalise and write one wave's 16 outputs: exactly two 16-byte buffer
@@ -492,7 +558,7 @@ __device__ inline void store_out(const Args &a, const Tile &t, int wave, int lan
 // workgroups sharing an L2 work on neighbouring tiles).  Per tile: attend,
 // barrier, issue the next tile's copies, store this tile's outputs, wait for
 // the copies only, barrier.
-template <typename T, int QY, int QX, int NCB, int RPC>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS>
 __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
 {
     using S = Shape<QY, QX, NCB, RPC>;
@@ -500,7 +566,8 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = a.lr;
-    const int nr = wave_rows(QY, RPC, a.ks);
+    const int ks = KS ? KS : a.ks;
+    const int nr = wave_rows(QY, RPC, ks);
 
     unsigned tile, step, end;
     if (a.xcd_split) {
@@ -515,36 +582,177 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
     }
     if (tile >= end) return;
 
-    float *b_gen = reinterpret_cast<float *>(smem + b_offset(lr, S::NC));
-    float *b_int = reinterpret_cast<float *>(smem + bi_offset(lr, S::NC, a.ks));
+    float *bt = reinterpret_cast<float *>(smem + b_offset(lr, S::NC));
     FragT qf;
     Tile t = tile_geometry<S::TY, S::TX, S::NC>(a, tile);
     int bias_head = t.h;
-    stage_bias<QY, QX, S::NC>(a, t.h, b_gen, b_int, nr, tid);
+    stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, ks, t.h, bt, nr, tid);
     stage_tile<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     while (true) {
         floatx4 o[2];
         float lsum;
-        attend_wave<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf, o, lsum);
+        attend_wave<T, QY, QX, NCB, RPC, KS>(a, t, smem, bt, lr, wave, lane, qf, o, lsum);
         const Tile done = t;
         const unsigned next = tile + step;
         __syncthreads();  // every wave is done reading the LDS copy
         if (next < end) {
             t = tile_geometry<S::TY, S::TX, S::NC>(a, next);
             if (t.h != bias_head) {  // rare: the tile list is head-major
-                stage_bias<QY, QX, S::NC>(a, t.h, b_gen, b_int, nr, tid);
+                stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, ks, t.h, bt, nr, tid);
                 bias_head = t.h;
             }
             stage_tile<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf);
         }
-        asm volatile("" ::: "memory");  // keep the stores after the copies just issued
         store_out<QY, QX>(a, done, wave, lane, o, lsum);
         if (next >= end) break;
-        NA2D_WAIT_VMCNT(2);  // the copies (older than the two stores) have landed
+        // loads and stores may retire out of order against each other, so
+        // only an empty counter proves the copies have landed
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         tile = next;
+    }
+}
+
+// Pipelined variant for a compile-time kernel size: while tile i is computed
+// from LDS, tile i+1's K/V halo rows and queries are already loading into
+// registers (plain buffer loads; out-of-map pixels return zeros), and are
+// written to LDS between two barriers once tile i is done.  The loads are
+// ordinary register loads, so the compiler's wait counts follow them exactly.
+template <int QY, int QX, int NCB, int LR>
+struct TileRegs {
+    static constexpr int ROWS = (LR + kWaves - 1) / kWaves;  // halo rows per wave (at most)
+    u32x4 k[ROWS][NCB], v[ROWS][NCB];
+    u32x4 q;  // this lane's query fragment
+};
+
+template <typename T, int QY, int QX, int NCB, int RPC, int LR>
+__device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, int lane,
+                                      TileRegs<QY, QX, NCB, LR> &rg)
+{
+    using S = Shape<QY, QX, NCB, RPC>;
+    const unsigned map_bytes = (unsigned)a.H * a.W * (kD * 2);
+    const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, t.map_base, kD * 2, map_bytes);
+    const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, t.map_base, kD * 2, map_bytes);
+    const int c_lane = lane >> 2, slot = lane & 3;
+#pragma unroll
+    for (int j = 0; j < TileRegs<QY, QX, NCB, LR>::ROWS; ++j) {
+        const int r = wave + kWaves * j;
+        const int gy = t.hy0 + r;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int c = 16 * cb + c_lane;
+            const int sl = slot ^ ((c >> 2) & 3);
+            const int gx = t.cx + c;
+            const unsigned off = r < LR && gy < a.H && gx < a.W
+                                     ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
+                                     : kOutOfRange;
+            rg.k[j][cb] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+            rg.v[j][cb] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        }
+    }
+    const int g = lane >> 4, qi = lane & 15;
+    const int y = min(t.y0 + QY * wave + qi / QX, a.H - 1);
+    const int x = min(t.x0 + qi % QX, a.W - 1);
+    const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, t.map_base, kD * 2, map_bytes);
+    rg.q = __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0, 0);
+}
+
+// the queries sit after the K and V halos: [wave][lane] 16-byte fragments
+__host__ __device__ constexpr unsigned q_frag_offset(int lr, int nc) { return 2u * lr * nc * 64u; }
+
+template <int QY, int QX, int NCB, int RPC, int LR>
+__device__ inline void write_tile_regs(unsigned char *smem, int wave, int lane,
+                                       const TileRegs<QY, QX, NCB, LR> &rg)
+{
+    using S = Shape<QY, QX, NCB, RPC>;
+    *reinterpret_cast<u32x4 *>(smem + q_frag_offset(LR, S::NC) + (unsigned)(wave * 64 + lane) * 16u) = rg.q;
+#pragma unroll
+    for (int j = 0; j < TileRegs<QY, QX, NCB, LR>::ROWS; ++j) {
+        const int r = wave + kWaves * j;
+        if (r < LR) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                unsigned char *dk = smem + (unsigned)(r * S::NC + 16 * cb) * 64u + 16u * lane;
+                *reinterpret_cast<u32x4 *>(dk) = rg.k[j][cb];
+                *reinterpret_cast<u32x4 *>(dk + halo_bytes(LR, S::NC)) = rg.v[j][cb];
+            }
+        }
+    }
+}
+
+template <typename T, int QY, int QX, int NCB, int RPC, int KS>
+__global__ __launch_bounds__(kThreads) void na2d_mfma_pipe_kernel(Args a)
+{
+    using S = Shape<QY, QX, NCB, RPC>;
+    using FragT = typename Frag<T>::type;
+    constexpr int NR = wave_rows(QY, RPC, KS);
+    constexpr int LR = S::TY + KS - 1 > NR ? S::TY + KS - 1 : NR;
+    constexpr unsigned HB = 2u * LR * S::NC * 64u + kThreads * 16u;  // K, V halos and queries
+    constexpr unsigned BF = bias_floats(S::CLS, KS, NR, QY, QX, S::NC, RPC);
+    __shared__ __align__(16) unsigned char halo[HB];
+    __shared__ __align__(16) float btab[BF];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    unsigned tile, step, end;
+    if (a.xcd_split) {
+        const unsigned xcd = blockIdx.x & 7u;
+        tile = (unsigned)(((uint64_t)a.ntiles * xcd) >> 3) + (blockIdx.x >> 3);
+        end = (unsigned)(((uint64_t)a.ntiles * (xcd + 1)) >> 3);
+        step = gridDim.x >> 3;
+    } else {
+        tile = blockIdx.x;
+        end = a.ntiles;
+        step = gridDim.x;
+    }
+    if (tile >= end) return;
+
+    TileRegs<QY, QX, NCB, LR> rg;
+    Tile t = tile_geometry<S::TY, S::TX, S::NC>(a, tile);
+    int bias_head = t.h;
+    stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, t.h, btab, NR, tid);
+    load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, t, wave, lane, rg);
+    __builtin_amdgcn_s_waitcnt(0);  // the first tile (and the bias table loads) complete
+    write_tile_regs<QY, QX, NCB, RPC, LR>(halo, wave, lane, rg);
+    unsigned next = tile + step;
+    Tile tn;
+    if (next < end) {
+        tn = tile_geometry<S::TY, S::TX, S::NC>(a, next);
+        load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, tn, wave, lane, rg);
+    }
+    __syncthreads();
+    const auto *qfrag = reinterpret_cast<const u32x4 *>(halo + q_frag_offset(LR, S::NC)) + tid;
+    while (true) {
+        // attend from LDS; the next tile is loading into `rg` meanwhile
+        floatx4 o[2];
+        float lsum;
+        const FragT qf = __builtin_bit_cast(FragT, *qfrag);
+        attend_wave<T, QY, QX, NCB, RPC, KS>(a, t, halo, btab, LR, wave, lane, qf, o, lsum);
+        const Tile done = t;
+        const bool more = next < end;
+        __syncthreads();  // every wave is done reading the halo (and the bias table)
+        if (more) {
+            if (tn.h != bias_head) {  // rare: the tile list is head-major
+                stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, tn.h, btab, NR, tid);
+                bias_head = tn.h;
+            }
+            // everything outstanding -- `rg` and the previous tile's stores --
+            // was issued a whole tile earlier, so an empty counter costs little
+            // (loads and stores may retire out of order, so nothing less will do)
+            __builtin_amdgcn_s_waitcnt(0);
+            write_tile_regs<QY, QX, NCB, RPC, LR>(halo, wave, lane, rg);
+        }
+        store_out<QY, QX>(a, done, wave, lane, o, lsum);
+        if (!more) break;
+        t = tn;
+        tile = next;
+        next = tile + step;
+        if (next < end) {
+            tn = tile_geometry<S::TY, S::TX, S::NC>(a, next);
+            load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, tn, wave, lane, rg);
+        }
+        __syncthreads();  // the new halo is visible
     }
 }
 
@@ -563,7 +771,7 @@ int device_cus()
     return cached_cus;
 }
 
-template <typename T, int QY, int QX, int NCB, int RPC>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS>
 hipError_t launch_cfg(const Problem &p, hipStream_t stream)
 {
     using S = Shape<QY, QX, NCB, RPC>;
@@ -586,8 +794,18 @@ hipError_t launch_cfg(const Problem &p, hipStream_t stream)
     const int nr = wave_rows(QY, RPC, p.ksize);
     a.lr = max(S::TY + p.ksize - 1, nr);
     a.c = 1.4426950408889634f / sqrtf((float)kD);
-    const size_t lds = lds_bytes(a.lr, S::NC, p.ksize, nr, QY, S::P);
-    auto kern = na2d_mfma_kernel<T, QY, QX, NCB, RPC>;
+    size_t lds = lds_bytes(a.lr, S::NC, bias_floats(S::CLS, p.ksize, nr, QY, QX, S::NC, RPC));
+    auto kern = na2d_mfma_kernel<T, QY, QX, NCB, RPC, KS>;
+    static const bool pipe_env = [] {
+        const char *e = getenv("NA2D_MFMA_PIPE");
+        return !(e && e[0] == '0');
+    }();
+    if constexpr (KS != 0) {
+        if (pipe_env) {
+            kern = na2d_mfma_pipe_kernel<T, QY, QX, NCB, RPC, KS>;
+            lds = 0;  // static LDS only
+        }
+    }
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -613,10 +831,10 @@ template <typename T>
 hipError_t launch_typed(const Problem &p, hipStream_t stream)
 {
     const int ks = p.ksize;
-    if (ks == 7) return launch_cfg<T, 2, 8, 1, 8>(p, stream);
-    if (ks <= 9) return launch_cfg<T, 2, 8, 1, 2>(p, stream);
-    if (ks <= 13) return launch_cfg<T, 4, 4, 1, 8>(p, stream);
-    return launch_cfg<T, 2, 8, 2, 2>(p, stream);
+    if (ks == 7) return launch_cfg<T, 2, 8, 1, 8, 7>(p, stream);
+    if (ks <= 9) return launch_cfg<T, 2, 8, 1, 2, 0>(p, stream);
+    if (ks <= 13) return launch_cfg<T, 4, 4, 1, 8, 0>(p, stream);
+    return launch_cfg<T, 2, 8, 2, 2, 0>(p, stream);
 }
 
 }  // namespace
