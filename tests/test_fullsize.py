@@ -1,0 +1,48 @@
+"""Every workload at its full size, launched as the benchmark launches it
+(automatic kernel selection, one launch over the whole batch), against the
+fp64 oracle on sampled outputs: one whole (b, head) map -- every border, corner
+and tile-seam position -- plus random queries from all maps.
+
+Tolerances as in the small-map parity tests: max-abs 1e-5 for float32
+inputs, 2e-3 for fp16/bf16 inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from vision_sliding_window_amd import na2d
+from vision_sliding_window_amd.inputs import WORKLOADS, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+def sampled_indices(w, n_random, seed):
+    """Flat [B, heads, H, W] query indices: the last map entirely, then
+    n_random distinct random queries."""
+    per_map = w.H * w.W
+    last = np.arange(w.queries - per_map, w.queries, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    rand = rng.choice(w.queries - per_map, size=min(n_random, w.queries - per_map), replace=False)
+    return np.concatenate([last, np.sort(rand).astype(np.int64)])
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_full_size_sampled(name):
+    w = WORKLOADS[name]
+    print("workload", name, flush=True)
+    x = workload_inputs(w, seed=0)
+    dev = torch.device("cuda")
+    out = na2d.forward(x.q.to(dev), x.k.to(dev), x.v.to(dev), x.rpb.to(dev), w.k)
+    torch.cuda.synchronize()
+    got = out.cpu().double().numpy().reshape(-1, w.d)
+    # properties of every output: finite, and a convex combination of values
+    assert np.isfinite(got).all()
+    assert np.abs(got).max() <= np.abs(x.v64).max() + TOL[w.dtype]
+    idx = sampled_indices(w, 4096, seed=1)
+    want = oracle.na2d_forward_sampled(x.q64, x.k64, x.v64, x.rpb64, w.k, idx)
+    err = np.abs(got[idx] - want).max()
+    print("  max|err| %.3g over %d sampled queries" % (err, idx.size), flush=True)
+    assert err <= TOL[w.dtype], "%s: max|err| %.3g > %.3g" % (name, err, TOL[w.dtype])

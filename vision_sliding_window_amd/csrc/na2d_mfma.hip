@@ -228,14 +228,33 @@ __device__ inline __amdgpu_buffer_rsrc_t map_rsrc(const void *base, int64_t map_
 //    a subtile none of whose queries is clamped, lane (qy, qx, g) reads
 //    element (row i, col c) at (QY-1-qy+i) * P + (QX-1-qx+c), which holds the
 //    bias of that offset or -inf where |dy| or |dx| exceeds k/2.
-// Every value of a pass is fetched before any is written.
+// Staging runs in two phases so that HBM is visited once, by every thread at
+// the same time: the head's (2k-1)^2 table is copied (scaled) into `raw`, an
+// LDS scratch area that is free at every call, and the tables are then
+// expanded from that copy.  Ends with a barrier (`raw` may be overwritten
+// afterwards, `bt` may be read).
+constexpr int kRawPerThread = (2 * NA2D_MFMA_MAX_KSIZE - 1) * (2 * NA2D_MFMA_MAX_KSIZE - 1) / kThreads + 1;
+
 template <int QY, int QX, int NC, int RPC, bool CLS>
-__device__ inline void stage_bias(const Args &a, int ks, int h, float *bt, int nr, int tid)
+__device__ inline void stage_bias(const Args &a, int ks, int h, float *bt, float *raw, int nr,
+                                  int tid)
 {
     constexpr int P = NC + QX - 1, PC = 2 * NC - 1;
-    constexpr int MAXV = 8;  // per-thread values per pass
-    const int nb = 2 * ks - 1, tw = 2 * ks, r = ks >> 1;
-    const float *rb = a.rpb ? a.rpb + (int64_t)h * nb * nb : nullptr;
+    const int nb = 2 * ks - 1, nraw = nb * nb, tw = 2 * ks, r = ks >> 1;
+    if (a.rpb) {
+        // every load is issued before the first is waited for: the indices are
+        // clamped rather than branched around
+        const float *rb = a.rpb + (int64_t)h * nraw;
+        float val[kRawPerThread];
+#pragma unroll
+        for (int e = 0; e < kRawPerThread; ++e) val[e] = rb[min(e * kThreads + tid, nraw - 1)];
+#pragma unroll
+        for (int e = 0; e < kRawPerThread; ++e)
+            if (e * kThreads + tid < nraw) raw[e * kThreads + tid] = val[e] * a.c;
+    } else {
+        for (int u = tid; u < nraw; u += kThreads) raw[u] = 0.f;
+    }
+    __syncthreads();
     int n1, n;
     if constexpr (CLS) {
         n1 = (int)class_floats(ks, PC);
@@ -244,40 +263,31 @@ __device__ inline void stage_bias(const Args &a, int ks, int h, float *bt, int n
         n1 = tw * tw;
         n = n1 + (nr + QY - 1) * P;
     }
-    for (int base = 0; base < n; base += MAXV * kThreads) {
-        float val[MAXV];
-#pragma unroll
-        for (int e = 0; e < MAXV; ++e) {
-            const int u = base + e * kThreads + tid;
-            int br = -1, bc = -1;
-            if constexpr (CLS) {
-                if (u < n1) {
-                    const int ex = u / (nb * PC), rem = u - ex * (nb * PC);
-                    br = rem / PC;
-                    bc = rem - br * PC - (NC - ks);
-                    if (bc < ks - 1 - ex || bc > 2 * ks - 2 - ex) br = -1;
-                }
-            } else {
-                if (u < n1) {
-                    br = u / tw;
-                    bc = u - br * tw;
-                    if (br >= nb || bc >= nb) br = -1;
-                } else if (u < n) {
-                    const int ui = u - n1, ai = ui / P, bi = ui - ai * P;
-                    br = ai + r - (QY - 1);
-                    bc = bi + r - (QX - 1);
-                    if (br < ks - 1 - r || br > ks - 1 + r || bc < ks - 1 - r || bc > ks - 1 + r)
-                        br = -1;
-                }
+    for (int u = tid; u < n; u += kThreads) {
+        int br = -1, bc = -1;
+        if constexpr (CLS) {
+            if (u < n1) {
+                const int ex = u / (nb * PC), rem = u - ex * (nb * PC);
+                br = rem / PC;
+                bc = rem - br * PC - (NC - ks);
+                if (bc < ks - 1 - ex || bc > 2 * ks - 2 - ex) br = -1;
             }
-            val[e] = br < 0 ? -__builtin_inff() : (rb ? rb[br * nb + bc] * a.c : 0.f);
+        } else {
+            if (u < n1) {
+                br = u / tw;
+                bc = u - br * tw;
+                if (br >= nb || bc >= nb) br = -1;
+            } else {
+                const int ui = u - n1, ai = ui / P, bi = ui - ai * P;
+                br = ai + r - (QY - 1);
+                bc = bi + r - (QX - 1);
+                if (br < ks - 1 - r || br > ks - 1 + r || bc < ks - 1 - r || bc > ks - 1 + r)
+                    br = -1;
+            }
         }
-#pragma unroll
-        for (int e = 0; e < MAXV; ++e) {
-            const int u = base + e * kThreads + tid;
-            if (u < n) bt[u] = val[e];
-        }
+        bt[u] = br < 0 ? -__builtin_inff() : raw[br * nb + bc];
     }
+    __syncthreads();
 }
 
 // Issue the copies of one tile's K/V halo into LDS (each wave its rows) and
@@ -586,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
     FragT qf;
     Tile t = tile_geometry<S::TY, S::TX, S::NC>(a, tile);
     int bias_head = t.h;
-    stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, ks, t.h, bt, nr, tid);
+    stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, ks, t.h, bt, reinterpret_cast<float *>(smem), nr, tid);
     stage_tile<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -600,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
         if (next < end) {
             t = tile_geometry<S::TY, S::TX, S::NC>(a, next);
             if (t.h != bias_head) {  // rare: the tile list is head-major
-                stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, ks, t.h, bt, nr, tid);
+                stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, ks, t.h, bt, reinterpret_cast<float *>(smem), nr, tid);
                 bias_head = t.h;
             }
             stage_tile<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf);
@@ -711,9 +721,10 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_pipe_kernel(Args a)
     TileRegs<QY, QX, NCB, LR> rg;
     Tile t = tile_geometry<S::TY, S::TX, S::NC>(a, tile);
     int bias_head = t.h;
-    stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, t.h, btab, NR, tid);
     load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, t, wave, lane, rg);
-    __builtin_amdgcn_s_waitcnt(0);  // the first tile (and the bias table loads) complete
+    // the halo area is free until the first tile is written into it
+    stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, t.h, btab, reinterpret_cast<float *>(halo), NR, tid);
+    __builtin_amdgcn_s_waitcnt(0);  // the first tile has landed
     write_tile_regs<QY, QX, NCB, RPC, LR>(halo, wave, lane, rg);
     unsigned next = tile + step;
     Tile tn;
@@ -734,7 +745,8 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_pipe_kernel(Args a)
         __syncthreads();  // every wave is done reading the halo (and the bias table)
         if (more) {
             if (tn.h != bias_head) {  // rare: the tile list is head-major
-                stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, tn.h, btab, NR, tid);
+                stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, tn.h, btab, reinterpret_cast<float *>(halo), NR,
+                                                       tid);
                 bias_head = tn.h;
             }
             // everything outstanding -- `rg` and the previous tile's stores --
@@ -816,6 +828,8 @@ hipError_t launch_cfg(const Problem &p, hipStream_t stream)
     if (e != hipSuccess) return e;
     const int cus = device_cus();
     if (per_cu <= 0 || cus <= 0) return hipErrorInvalidConfiguration;
+    // one workgroup per resident slot (measured faster than fewer, evenly
+    // loaded workgroups: the memory system wants every slot's loads in flight)
     uint64_t grid = (uint64_t)cus * per_cu;
     if (grid > ntiles) grid = ntiles;
     a.xcd_split = 0;
