@@ -229,27 +229,39 @@ __device__ inline __amdgpu_buffer_rsrc_t map_rsrc(const void *base, int64_t map_
 //    element (row i, col c) at (QY-1-qy+i) * P + (QX-1-qx+c), which holds the
 //    bias of that offset or -inf where |dy| or |dx| exceeds k/2.
 // Staging runs in two phases so that HBM is visited once, by every thread at
-// the same time: the head's (2k-1)^2 table is copied (scaled) into `raw`, an
-// LDS scratch area that is free at every call, and the tables are then
-// expanded from that copy.  Ends with a barrier (`raw` may be overwritten
-// afterwards, `bt` may be read).
+// the same time: load_raw_bias issues the loads of the head's (2k-1)^2 table
+// (indices clamped rather than branched around, so no load waits for
+// another), and stage_bias writes them, scaled, into `raw` -- an LDS scratch
+// area that is free at every call -- then expands the tables from that copy.
+// stage_bias ends with a barrier (`raw` may be overwritten afterwards, `bt`
+// may be read).
 constexpr int kRawPerThread = (2 * NA2D_MFMA_MAX_KSIZE - 1) * (2 * NA2D_MFMA_MAX_KSIZE - 1) / kThreads + 1;
 
-template <int QY, int QX, int NC, int RPC, bool CLS>
-__device__ inline void stage_bias(const Args &a, int ks, int h, float *bt, float *raw, int nr,
-                                  int tid)
+// raw values per thread for a compile-time kernel size (0: any size)
+__host__ __device__ constexpr int raw_per_thread(int ks)
+{
+    return ks ? (2 * ks - 1) * (2 * ks - 1) / kThreads + 1 : kRawPerThread;
+}
+
+template <int NV>
+__device__ inline void load_raw_bias(const Args &a, int ks, int h, int tid, float (&val)[NV])
+{
+    if (!a.rpb) return;
+    const int nb = 2 * ks - 1, nraw = nb * nb;
+    const float *rb = a.rpb + (int64_t)h * nraw;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) val[e] = rb[min(e * kThreads + tid, nraw - 1)];
+}
+
+template <int QY, int QX, int NC, int RPC, bool CLS, int NV>
+__device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV], float *bt,
+                                  float *raw, int nr, int tid)
 {
     constexpr int P = NC + QX - 1, PC = 2 * NC - 1;
     const int nb = 2 * ks - 1, nraw = nb * nb, tw = 2 * ks, r = ks >> 1;
     if (a.rpb) {
-        // every load is issued before the first is waited for: the indices are
-        // clamped rather than branched around
-        const float *rb = a.rpb + (int64_t)h * nraw;
-        float val[kRawPerThread];
 #pragma unroll
-        for (int e = 0; e < kRawPerThread; ++e) val[e] = rb[min(e * kThreads + tid, nraw - 1)];
-#pragma unroll
-        for (int e = 0; e < kRawPerThread; ++e)
+        for (int e = 0; e < NV; ++e)
             if (e * kThreads + tid < nraw) raw[e * kThreads + tid] = val[e] * a.c;
     } else {
         for (int u = tid; u < nraw; u += kThreads) raw[u] = 0.f;
@@ -288,6 +300,15 @@ __device__ inline void stage_bias(const Args &a, int ks, int h, float *bt, float
         bt[u] = br < 0 ? -__builtin_inff() : raw[br * nb + bc];
     }
     __syncthreads();
+}
+
+template <int QY, int QX, int NC, int RPC, bool CLS>
+__device__ inline void stage_bias(const Args &a, int ks, int h, float *bt, float *raw, int nr,
+                                  int tid)
+{
+    float val[kRawPerThread];
+    load_raw_bias(a, ks, h, tid, val);
+    stage_bias<QY, QX, NC, RPC, CLS>(a, ks, val, bt, raw, nr, tid);
 }
 
 // Issue the copies of one tile's K/V halo into LDS (each wave its rows) and
@@ -637,9 +658,11 @@ struct TileRegs {
     u32x4 q;  // this lane's query fragment
 };
 
+// With `live` false every offset is out of range: the loads still issue (so
+// the wait counts do not depend on it) but return zeros without touching memory.
 template <typename T, int QY, int QX, int NCB, int RPC, int LR>
 __device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, int lane,
-                                      TileRegs<QY, QX, NCB, LR> &rg)
+                                      TileRegs<QY, QX, NCB, LR> &rg, bool live = true)
 {
     using S = Shape<QY, QX, NCB, RPC>;
     const unsigned map_bytes = (unsigned)a.H * a.W * (kD * 2);
@@ -655,7 +678,7 @@ __device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, in
             const int c = 16 * cb + c_lane;
             const int sl = slot ^ ((c >> 2) & 3);
             const int gx = t.cx + c;
-            const unsigned off = r < LR && gy < a.H && gx < a.W
+            const unsigned off = live && r < LR && gy < a.H && gx < a.W
                                      ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
                                      : kOutOfRange;
             rg.k[j][cb] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
@@ -666,7 +689,8 @@ __device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, in
     const int y = min(t.y0 + QY * wave + qi / QX, a.H - 1);
     const int x = min(t.x0 + qi % QX, a.W - 1);
     const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, t.map_base, kD * 2, map_bytes);
-    rg.q = __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0, 0);
+    rg.q = __builtin_amdgcn_raw_buffer_load_b128(
+        rq, live ? (unsigned)(y * a.W + x) * 64u + 16u * g : kOutOfRange, 0, 0);
 }
 
 // the queries sit after the K and V halos: [wave][lane] 16-byte fragments
@@ -718,20 +742,23 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_pipe_kernel(Args a)
     }
     if (tile >= end) return;
 
-    TileRegs<QY, QX, NCB, LR> rg;
+    // Prologue: with no store issued yet, loads retire in order, so the bias
+    // table, the first tile and the second tile can all be in flight at once
+    // and each be waited for alone.
+    constexpr int NV = raw_per_thread(KS);
+    TileRegs<QY, QX, NCB, LR> rg0, rg;
     Tile t = tile_geometry<S::TY, S::TX, S::NC>(a, tile);
     int bias_head = t.h;
-    load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, t, wave, lane, rg);
-    // the halo area is free until the first tile is written into it
-    stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, t.h, btab, reinterpret_cast<float *>(halo), NR, tid);
-    __builtin_amdgcn_s_waitcnt(0);  // the first tile has landed
-    write_tile_regs<QY, QX, NCB, RPC, LR>(halo, wave, lane, rg);
+    float raw_bias[NV];
+    load_raw_bias(a, KS, t.h, tid, raw_bias);
+    load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, t, wave, lane, rg0);
     unsigned next = tile + step;
-    Tile tn;
-    if (next < end) {
-        tn = tile_geometry<S::TY, S::TX, S::NC>(a, next);
-        load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, tn, wave, lane, rg);
-    }
+    Tile tn = tile_geometry<S::TY, S::TX, S::NC>(a, next < end ? next : tile);
+    load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, tn, wave, lane, rg, next < end);
+    // the halo area is free until the first tile is written into it
+    stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, raw_bias, btab, reinterpret_cast<float *>(halo),
+                                           NR, tid);
+    write_tile_regs<QY, QX, NCB, RPC, LR>(halo, wave, lane, rg0);
     __syncthreads();
     const auto *qfrag = reinterpret_cast<const u32x4 *>(halo + q_frag_offset(LR, S::NC)) + tid;
     while (true) {
