@@ -5,18 +5,16 @@
 // clamped ksize x ksize window, logits (q.k + B) / sqrt(d), softmax over the
 // window, weighted sum of the values.
 //
-// How.  Persistent workgroups of 4 waves walk a list of query tiles of
-// TY x TX = (4 QY) x QX queries; each wave owns one QY x QX = 16-query subtile.
+// How.  Persistent workgroups of NW waves walk a list of query tiles of
+// TY x TX = (NW QY) x QX queries; each wave owns one QY x QX = 16-query subtile.
 //  1. Staging.  The tile's key/value halo -- the union of its queries'
-//     windows, at most TY + ksize - 1 rows by NC = 16 NCB columns -- is copied
-//     HBM -> LDS with buffer_load_dwordx4 ... lds (each lane's 16 bytes land
-//     at M0 + 16 lane; no VGPRs), as [row][col][d] for both K and V.  The
-//     16-byte d-slice s of pixel column c sits at slot s ^ ((c >> 2) & 3) so
-//     the reads below are free of bank conflicts.  Pixels outside the map get
-//     an out-of-range buffer offset and so arrive as zeros.  The queries go
-//     straight to registers.  This is the tiled design of the paperlayer
-//     summary's appendix A.4 (a query tile plus a key tile of side tq + k - 1
-//     in on-chip memory), re-shaped for 64-lane waves and LDS DMA.
+//     windows, at most TY + ksize - 1 rows by NC = 16 NCB columns -- goes to
+//     LDS as [row][col][d] for both K and V.  The 16-byte d-slice s of pixel
+//     column c sits at slot s ^ ((c >> 2) & 3) so the reads below are free of
+//     bank conflicts.  Pixels outside the map get an out-of-range buffer
+//     offset and so arrive as zeros.  This is the tiled design of the
+//     paperlayer summary's appendix A.4 (a query tile plus a key tile of side
+//     tq + k - 1 in on-chip memory), re-shaped for 64-lane waves.
 //  2. Logits.  The wave's candidate keys are NR halo rows by NC columns, in
 //     blocks of 16 (one row, 16 consecutive columns).  For a block,
 //     S^T = K_block Q^T is one v_mfma_f32_16x16x32 (d = 32 is the
@@ -35,8 +33,13 @@
 //     ~16 bits either way.
 //  5. out = O / sum in fp32 with 16-byte buffer stores (out-of-map lanes get
 //     an out-of-range offset and are dropped).
-// Pipelining: the next tile's copies are issued before this tile's stores,
-// and the wait for them (vmcnt(2)) leaves the two stores in flight.
+// Two kernels share steps 2-5.  na2d_mfma_kernel (any kernel size) copies the
+// halo HBM -> LDS with buffer_load ... lds (no VGPRs) and then waits for it;
+// na2d_mfma_pipe_kernel (a compile-time kernel size) loads the next tile's
+// halo into registers while the current tile is computed, and writes it to
+// LDS between two barriers.  Either way each iteration drains the vector
+// memory counter completely: loads and stores may retire out of order against
+// each other, so a partial count would not prove the halo had landed.
 // No ksize^2-wide tensor ever leaves the chip.
 #include "na2d.h"
 #include "na2d_launch.h"
@@ -44,7 +47,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <cstdlib>
 
 namespace na2d {
 namespace {
@@ -64,7 +66,7 @@ typedef __attribute__((address_space(3))) const float lds_cf32;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int kD = 32;        // head dim handled here
-constexpr int kWaves = 4;     // waves per workgroup, stacked vertically
+constexpr int kWaves = 4;     // waves per workgroup of the general kernel, stacked vertically
 constexpr int kThreads = 64 * kWaves;
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr unsigned kOutOfRange = 0x7ffffff0u;  // byte offset past any map: loads 0, stores dropped
@@ -130,9 +132,10 @@ struct Args {
     float c;               // log2(e) / sqrt(d)
 };
 
-template <int QY, int QX, int NCB, int RPC>
+template <int QY, int QX, int NCB, int RPC, int NW = kWaves>
 struct Shape {
-    static constexpr int TY = QY * kWaves;          // tile rows
+    static constexpr int NT = 64 * NW;              // threads per workgroup
+    static constexpr int TY = QY * NW;              // tile rows
     static constexpr int TX = QX;                   // tile cols
     static constexpr int NC = 16 * NCB;             // halo cols held in LDS
     static constexpr int BPC = RPC * NCB;           // key blocks per chunk
@@ -235,25 +238,24 @@ __device__ inline __amdgpu_buffer_rsrc_t map_rsrc(const void *base, int64_t map_
 // area that is free at every call -- then expands the tables from that copy.
 // stage_bias ends with a barrier (`raw` may be overwritten afterwards, `bt`
 // may be read).
-constexpr int kRawPerThread = (2 * NA2D_MFMA_MAX_KSIZE - 1) * (2 * NA2D_MFMA_MAX_KSIZE - 1) / kThreads + 1;
-
 // raw values per thread for a compile-time kernel size (0: any size)
-__host__ __device__ constexpr int raw_per_thread(int ks)
+__host__ __device__ constexpr int raw_per_thread(int ks, int nt)
 {
-    return ks ? (2 * ks - 1) * (2 * ks - 1) / kThreads + 1 : kRawPerThread;
+    const int k = ks ? ks : NA2D_MFMA_MAX_KSIZE;
+    return (2 * k - 1) * (2 * k - 1) / nt + 1;
 }
 
-template <int NV>
+template <int NT, int NV>
 __device__ inline void load_raw_bias(const Args &a, int ks, int h, int tid, float (&val)[NV])
 {
     if (!a.rpb) return;
     const int nb = 2 * ks - 1, nraw = nb * nb;
     const float *rb = a.rpb + (int64_t)h * nraw;
 #pragma unroll
-    for (int e = 0; e < NV; ++e) val[e] = rb[min(e * kThreads + tid, nraw - 1)];
+    for (int e = 0; e < NV; ++e) val[e] = rb[min(e * NT + tid, nraw - 1)];
 }
 
-template <int QY, int QX, int NC, int RPC, bool CLS, int NV>
+template <int QY, int QX, int NC, int RPC, bool CLS, int NT, int NV>
 __device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV], float *bt,
                                   float *raw, int nr, int tid)
 {
@@ -262,9 +264,9 @@ __device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV],
     if (a.rpb) {
 #pragma unroll
         for (int e = 0; e < NV; ++e)
-            if (e * kThreads + tid < nraw) raw[e * kThreads + tid] = val[e] * a.c;
+            if (e * NT + tid < nraw) raw[e * NT + tid] = val[e] * a.c;
     } else {
-        for (int u = tid; u < nraw; u += kThreads) raw[u] = 0.f;
+        for (int u = tid; u < nraw; u += NT) raw[u] = 0.f;
     }
     __syncthreads();
     int n1, n;
@@ -275,7 +277,7 @@ __device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV],
         n1 = tw * tw;
         n = n1 + (nr + QY - 1) * P;
     }
-    for (int u = tid; u < n; u += kThreads) {
+    for (int u = tid; u < n; u += NT) {
         int br = -1, bc = -1;
         if constexpr (CLS) {
             if (u < n1) {
@@ -302,13 +304,13 @@ __device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV],
     __syncthreads();
 }
 
-template <int QY, int QX, int NC, int RPC, bool CLS>
+template <int QY, int QX, int NC, int RPC, bool CLS, int NT = kThreads>
 __device__ inline void stage_bias(const Args &a, int ks, int h, float *bt, float *raw, int nr,
                                   int tid)
 {
-    float val[kRawPerThread];
-    load_raw_bias(a, ks, h, tid, val);
-    stage_bias<QY, QX, NC, RPC, CLS>(a, ks, val, bt, raw, nr, tid);
+    float val[raw_per_thread(0, NT)];
+    load_raw_bias<NT>(a, ks, h, tid, val);
+    stage_bias<QY, QX, NC, RPC, CLS, NT>(a, ks, val, bt, raw, nr, tid);
 }
 
 // Issue the copies of one tile's K/V halo into LDS (each wave its rows) and
@@ -651,27 +653,27 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
 // registers (plain buffer loads; out-of-map pixels return zeros), and are
 // written to LDS between two barriers once tile i is done.  The loads are
 // ordinary register loads, so the compiler's wait counts follow them exactly.
-template <int QY, int QX, int NCB, int LR>
+template <int QY, int QX, int NCB, int LR, int NW>
 struct TileRegs {
-    static constexpr int ROWS = (LR + kWaves - 1) / kWaves;  // halo rows per wave (at most)
+    static constexpr int ROWS = (LR + NW - 1) / NW;  // halo rows per wave (at most)
     u32x4 k[ROWS][NCB], v[ROWS][NCB];
     u32x4 q;  // this lane's query fragment
 };
 
 // With `live` false every offset is out of range: the loads still issue (so
 // the wait counts do not depend on it) but return zeros without touching memory.
-template <typename T, int QY, int QX, int NCB, int RPC, int LR>
+template <typename T, int QY, int QX, int NCB, int RPC, int LR, int NW>
 __device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, int lane,
-                                      TileRegs<QY, QX, NCB, LR> &rg, bool live = true)
+                                      TileRegs<QY, QX, NCB, LR, NW> &rg, bool live = true)
 {
-    using S = Shape<QY, QX, NCB, RPC>;
+    using S = Shape<QY, QX, NCB, RPC, NW>;
     const unsigned map_bytes = (unsigned)a.H * a.W * (kD * 2);
     const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, t.map_base, kD * 2, map_bytes);
     const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, t.map_base, kD * 2, map_bytes);
     const int c_lane = lane >> 2, slot = lane & 3;
 #pragma unroll
-    for (int j = 0; j < TileRegs<QY, QX, NCB, LR>::ROWS; ++j) {
-        const int r = wave + kWaves * j;
+    for (int j = 0; j < TileRegs<QY, QX, NCB, LR, NW>::ROWS; ++j) {
+        const int r = wave + NW * j;
         const int gy = t.hy0 + r;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
@@ -696,15 +698,15 @@ __device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, in
 // the queries sit after the K and V halos: [wave][lane] 16-byte fragments
 __host__ __device__ constexpr unsigned q_frag_offset(int lr, int nc) { return 2u * lr * nc * 64u; }
 
-template <int QY, int QX, int NCB, int RPC, int LR>
+template <int QY, int QX, int NCB, int RPC, int LR, int NW>
 __device__ inline void write_tile_regs(unsigned char *smem, int wave, int lane,
-                                       const TileRegs<QY, QX, NCB, LR> &rg)
+                                       const TileRegs<QY, QX, NCB, LR, NW> &rg)
 {
-    using S = Shape<QY, QX, NCB, RPC>;
+    using S = Shape<QY, QX, NCB, RPC, NW>;
     *reinterpret_cast<u32x4 *>(smem + q_frag_offset(LR, S::NC) + (unsigned)(wave * 64 + lane) * 16u) = rg.q;
 #pragma unroll
-    for (int j = 0; j < TileRegs<QY, QX, NCB, LR>::ROWS; ++j) {
-        const int r = wave + kWaves * j;
+    for (int j = 0; j < TileRegs<QY, QX, NCB, LR, NW>::ROWS; ++j) {
+        const int r = wave + NW * j;
         if (r < LR) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
@@ -716,14 +718,14 @@ __device__ inline void write_tile_regs(unsigned char *smem, int wave, int lane,
     }
 }
 
-template <typename T, int QY, int QX, int NCB, int RPC, int KS>
-__global__ __launch_bounds__(kThreads) void na2d_mfma_pipe_kernel(Args a)
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW>
+__global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
 {
-    using S = Shape<QY, QX, NCB, RPC>;
+    using S = Shape<QY, QX, NCB, RPC, NW>;
     using FragT = typename Frag<T>::type;
     constexpr int NR = wave_rows(QY, RPC, KS);
     constexpr int LR = S::TY + KS - 1 > NR ? S::TY + KS - 1 : NR;
-    constexpr unsigned HB = 2u * LR * S::NC * 64u + kThreads * 16u;  // K, V halos and queries
+    constexpr unsigned HB = 2u * LR * S::NC * 64u + S::NT * 16u;  // K, V halos and queries
     constexpr unsigned BF = bias_floats(S::CLS, KS, NR, QY, QX, S::NC, RPC);
     __shared__ __align__(16) unsigned char halo[HB];
     __shared__ __align__(16) float btab[BF];
@@ -745,35 +747,38 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_pipe_kernel(Args a)
     // Prologue: with no store issued yet, loads retire in order, so the bias
     // table, the first tile and the second tile can all be in flight at once
     // and each be waited for alone.
-    constexpr int NV = raw_per_thread(KS);
-    TileRegs<QY, QX, NCB, LR> rg0, rg;
+    constexpr int NV = raw_per_thread(KS, S::NT);
+    TileRegs<QY, QX, NCB, LR, NW> rg0, rg;
     Tile t = tile_geometry<S::TY, S::TX, S::NC>(a, tile);
     int bias_head = t.h;
     float raw_bias[NV];
-    load_raw_bias(a, KS, t.h, tid, raw_bias);
+    load_raw_bias<S::NT>(a, KS, t.h, tid, raw_bias);
     load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, t, wave, lane, rg0);
     unsigned next = tile + step;
     Tile tn = tile_geometry<S::TY, S::TX, S::NC>(a, next < end ? next : tile);
     load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, tn, wave, lane, rg, next < end);
     // the halo area is free until the first tile is written into it
-    stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, raw_bias, btab, reinterpret_cast<float *>(halo),
-                                           NR, tid);
+    stage_bias<QY, QX, S::NC, RPC, S::CLS, S::NT>(a, KS, raw_bias, btab,
+                                                  reinterpret_cast<float *>(halo), NR, tid);
     write_tile_regs<QY, QX, NCB, RPC, LR>(halo, wave, lane, rg0);
     __syncthreads();
     const auto *qfrag = reinterpret_cast<const u32x4 *>(halo + q_frag_offset(LR, S::NC)) + tid;
     while (true) {
         // attend from LDS; the next tile is loading into `rg` meanwhile
-        floatx4 o[2];
-        float lsum;
-        const FragT qf = __builtin_bit_cast(FragT, *qfrag);
-        attend_wave<T, QY, QX, NCB, RPC, KS>(a, t, halo, btab, LR, wave, lane, qf, o, lsum);
+        floatx4 o[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+        float lsum = 1.f;
+        if (t.y0 + QY * wave < a.H) {  // the bottom tile row may leave whole waves idle
+            const FragT qf = __builtin_bit_cast(FragT, *qfrag);
+            attend_wave<T, QY, QX, NCB, RPC, KS>(a, t, halo, btab, LR, wave, lane, qf, o, lsum);
+        }
         const Tile done = t;
         const bool more = next < end;
         __syncthreads();  // every wave is done reading the halo (and the bias table)
         if (more) {
             if (tn.h != bias_head) {  // rare: the tile list is head-major
-                stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, KS, tn.h, btab, reinterpret_cast<float *>(halo), NR,
-                                                       tid);
+                stage_bias<QY, QX, S::NC, RPC, S::CLS, S::NT>(a, KS, tn.h, btab,
+                                                              reinterpret_cast<float *>(halo), NR,
+                                                              tid);
                 bias_head = tn.h;
             }
             // everything outstanding -- `rg` and the previous tile's stores --
@@ -810,11 +815,11 @@ int device_cus()
     return cached_cus;
 }
 
-template <typename T, int QY, int QX, int NCB, int RPC, int KS>
-hipError_t launch_cfg(const Problem &p, hipStream_t stream)
+// Arguments and tile counts for a tile shape S; false if the tile list does
+// not fit 32 bits.
+template <typename S, int QY, int RPC>
+bool make_args(const Problem &p, Args &a)
 {
-    using S = Shape<QY, QX, NCB, RPC>;
-    Args a;
     a.q = p.q;
     a.k = p.k;
     a.v = p.v;
@@ -828,54 +833,72 @@ hipError_t launch_cfg(const Problem &p, hipStream_t stream)
     a.tiles_x = (p.W + S::TX - 1) / S::TX;
     a.tiles_y = (p.H + S::TY - 1) / S::TY;
     const uint64_t ntiles = (uint64_t)p.B * p.heads * a.tiles_x * a.tiles_y;
-    if (ntiles == 0 || ntiles > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    if (ntiles == 0 || ntiles > 0x7fffffffull) return false;
     a.ntiles = (unsigned)ntiles;
-    const int nr = wave_rows(QY, RPC, p.ksize);
-    a.lr = max(S::TY + p.ksize - 1, nr);
+    a.lr = max(S::TY + p.ksize - 1, wave_rows(QY, RPC, p.ksize));
     a.c = 1.4426950408889634f / sqrtf((float)kD);
-    size_t lds = lds_bytes(a.lr, S::NC, bias_floats(S::CLS, p.ksize, nr, QY, QX, S::NC, RPC));
-    auto kern = na2d_mfma_kernel<T, QY, QX, NCB, RPC, KS>;
-    static const bool pipe_env = [] {
-        const char *e = getenv("NA2D_MFMA_PIPE");
-        return !(e && e[0] == '0');
-    }();
-    if constexpr (KS != 0) {
-        if (pipe_env) {
-            kern = na2d_mfma_pipe_kernel<T, QY, QX, NCB, RPC, KS>;
-            lds = 0;  // static LDS only
-        }
-    }
+    return true;
+}
+
+// One workgroup per resident slot (measured faster than fewer, evenly loaded
+// workgroups: the memory system wants every slot's loads in flight), each
+// XCD given its own contiguous tile range when there are enough workgroups.
+template <typename K>
+hipError_t launch_persistent(K kern, Args &a, int threads, size_t lds, hipStream_t stream)
+{
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds);
     if (e != hipSuccess) return e;
     const int cus = device_cus();
     if (per_cu <= 0 || cus <= 0) return hipErrorInvalidConfiguration;
-    // one workgroup per resident slot (measured faster than fewer, evenly
-    // loaded workgroups: the memory system wants every slot's loads in flight)
     uint64_t grid = (uint64_t)cus * per_cu;
-    if (grid > ntiles) grid = ntiles;
+    if (grid > a.ntiles) grid = a.ntiles;
     a.xcd_split = 0;
-    if (grid >= 64) {  // enough workgroups to give every XCD its own tile range
+    if (grid >= 64) {
         grid &= ~7ull;
         a.xcd_split = 1;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, stream, a);
     return hipGetLastError();
+}
+
+// General kernel sizes: the LDS-DMA kernel with 4 waves per workgroup.
+template <typename T, int QY, int QX, int NCB, int RPC>
+hipError_t launch_dma(const Problem &p, hipStream_t stream)
+{
+    using S = Shape<QY, QX, NCB, RPC>;
+    Args a;
+    if (!make_args<S, QY, RPC>(p, a)) return hipErrorInvalidConfiguration;
+    const int nr = wave_rows(QY, RPC, p.ksize);
+    const size_t lds =
+        lds_bytes(a.lr, S::NC, bias_floats(S::CLS, p.ksize, nr, QY, QX, S::NC, RPC));
+    return launch_persistent(na2d_mfma_kernel<T, QY, QX, NCB, RPC, 0>, a, S::NT, lds, stream);
+}
+
+// A compile-time kernel size: the register-prefetch kernel with NW waves.
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW>
+hipError_t launch_pipe(const Problem &p, hipStream_t stream)
+{
+    using S = Shape<QY, QX, NCB, RPC, NW>;
+    Args a;
+    if (!make_args<S, QY, RPC>(p, a)) return hipErrorInvalidConfiguration;
+    return launch_persistent(na2d_mfma_pipe_kernel<T, QY, QX, NCB, RPC, KS, NW>, a, S::NT, 0,
+                             stream);
 }
 
 template <typename T>
 hipError_t launch_typed(const Problem &p, hipStream_t stream)
 {
     const int ks = p.ksize;
-    if (ks == 7) return launch_cfg<T, 2, 8, 1, 8, 7>(p, stream);
-    if (ks <= 9) return launch_cfg<T, 2, 8, 1, 2, 0>(p, stream);
-    if (ks <= 13) return launch_cfg<T, 4, 4, 1, 8, 0>(p, stream);
-    return launch_cfg<T, 2, 8, 2, 2, 0>(p, stream);
+    if (ks == 7) return launch_pipe<T, 2, 8, 1, 8, 7, 4>(p, stream);
+    if (ks <= 9) return launch_dma<T, 2, 8, 1, 2>(p, stream);
+    if (ks <= 13) return launch_dma<T, 4, 4, 1, 8>(p, stream);
+    return launch_dma<T, 2, 8, 2, 2>(p, stream);
 }
 
 }  // namespace
