@@ -21,6 +21,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "na2d_oracle.c")
 LIBRARY = os.path.join(_HERE, "libna2d_oracle.so")
+ND_SOURCE = os.path.join(_HERE, "na_nd_oracle.c")
+ND_LIBRARY = os.path.join(_HERE, "libna_nd_oracle.so")
+
+NA, SASA = 0, 1  # window modes of the N-axis oracle
 
 
 def compile_oracle(src: str, out: str) -> str:
@@ -36,6 +40,8 @@ def compile_oracle(src: str, out: str) -> str:
 def build(force: bool = True) -> str:
     if force or not os.path.exists(LIBRARY):
         compile_oracle(SOURCE, LIBRARY)
+    if force or not os.path.exists(ND_LIBRARY):
+        compile_oracle(ND_SOURCE, ND_LIBRARY)
     return LIBRARY
 
 
@@ -121,3 +127,86 @@ def na2d_forward(q, k, v, rpb, ksize: int, nthreads: int = 0) -> np.ndarray:
 
 def na2d_forward_sampled(q, k, v, rpb, ksize: int, idx, nthreads: int = 0) -> np.ndarray:
     return default().na2d_forward_sampled(q, k, v, rpb, ksize, idx, nthreads)
+
+
+class OracleND:
+    """ctypes front of the N-axis oracle (na_nd_oracle.c): NA over 1, 2 or 3
+    axes (mode NA) and SASA windows on a zero-padded input (mode SASA)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.na_nd_window_start.argtypes = [I, I, I, I]
+        lib.na_nd_window_start.restype = I
+        lib.na_nd_oracle_f64.argtypes = [P, P, P, P, P, I64, P] + [I] * 11
+        lib.na_nd_oracle_f64.restype = I
+        self.lib = lib
+        self.path = path
+
+    def window_start(self, i: int, k: int, L: int, mode: int = NA) -> int:
+        return self.lib.na_nd_window_start(i, k, L, mode)
+
+    def forward(self, q, k, v, rpb, ksizes, mode: int = NA, idx=None, nthreads: int = 0):
+        """q, k, v: [B, heads, L0, L1, L2, d]; rpb: [heads, 2k0-1, 2k1-1, 2k2-1] or None.
+        Returns [B, heads, L0, L1, L2, d], or [n, d] for the linear query indices idx."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        assert q.ndim == 6 and q.shape == k.shape == v.shape
+        B, heads, L0, L1, L2, d = q.shape
+        k0, k1, k2 = ksizes
+        if rpb is not None:
+            rpb = _f64(rpb)
+            assert rpb.shape == (heads, 2 * k0 - 1, 2 * k1 - 1, 2 * k2 - 1)
+        if idx is None:
+            out = np.empty_like(q)
+            n = q.size // d
+        else:
+            idx = np.ascontiguousarray(idx, dtype=np.int64)
+            out = np.empty((idx.size, d), dtype=np.float64)
+            n = idx.size
+        rc = self.lib.na_nd_oracle_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(idx), n,
+                                       _ptr(out), B, heads, L0, L1, L2, d, k0, k1, k2, mode,
+                                       nthreads)
+        if rc != 0:
+            raise ValueError("oracle rejected sizes %s k=%s mode=%d" % (q.shape, ksizes, mode))
+        return out
+
+
+_default_nd = None
+
+
+def default_nd() -> OracleND:
+    global _default_nd
+    if _default_nd is None:
+        if not os.path.exists(ND_LIBRARY):
+            build()
+        _default_nd = OracleND(ND_LIBRARY)
+    return _default_nd
+
+
+def na1d_forward(q, k, v, rpb, ksize: int, idx=None, nthreads: int = 0, orc=None):
+    """NA1D: q, k, v [B, heads, L, d], rpb [heads, 2k-1] or None."""
+    orc = orc or default_nd()
+    B, heads, L, d = q.shape
+    sh = (B, heads, 1, 1, L, d)
+    r = None if rpb is None else np.asarray(rpb).reshape(heads, 1, 1, 2 * ksize - 1)
+    out = orc.forward(np.reshape(q, sh), np.reshape(k, sh), np.reshape(v, sh), r, (1, 1, ksize),
+                      NA, idx, nthreads)
+    return out if idx is not None else out.reshape(q.shape)
+
+
+def na3d_forward(q, k, v, rpb, ksize: int, idx=None, nthreads: int = 0, orc=None):
+    """NA3D: q, k, v [B, heads, D, H, W, d], rpb [heads, 2k-1, 2k-1, 2k-1] or None."""
+    orc = orc or default_nd()
+    return orc.forward(q, k, v, rpb, (ksize, ksize, ksize), NA, idx, nthreads)
+
+
+def sasa2d_forward(q, k, v, rpb, ksize: int, idx=None, nthreads: int = 0, orc=None):
+    """SASA on a 2D map (centred k x k windows, zero padding): q, k, v
+    [B, heads, H, W, d], rpb [heads, 2k-1, 2k-1] or None."""
+    orc = orc or default_nd()
+    B, heads, H, W, d = q.shape
+    sh = (B, heads, 1, H, W, d)
+    r = None if rpb is None else np.asarray(rpb).reshape(heads, 1, 2 * ksize - 1, 2 * ksize - 1)
+    out = orc.forward(np.reshape(q, sh), np.reshape(k, sh), np.reshape(v, sh), r, (1, ksize, ksize),
+                      SASA, idx, nthreads)
+    return out if idx is not None else out.reshape(q.shape)
