@@ -1,10 +1,12 @@
-"""Benchmark of the fused NA2D forward on one MI355X.
+"""Benchmark of the fused Neighborhood Attention forward on one MI355X.
 
-One step = one fused NA2D forward launch over the whole batch of the
-NAT-Tiny stage-1 workload (B=32, 2 heads, 56x56, d=32, k=7, fp16 inputs,
-fp32 output), inputs already resident in HBM.  The timed region rotates over
-enough input/output sets (>= 1 GiB) that the 256 MB Infinity Cache cannot hold
-them, so the figure is an HBM figure.  Prints one JSON line.
+One step = one fused forward launch over the whole batch of a workload, by
+default NAT-Tiny stage 1 (B=32, 2 heads, 56x56, d=32, k=7, fp16 inputs, fp32
+output), inputs already resident in HBM.  `--workload` also takes the other
+NA2D shapes and the NA1D, NA3D and SASA workloads (see inputs.WORKLOADS).  The
+timed region rotates over enough input/output sets (>= 1 GiB) that the 256 MB
+Infinity Cache cannot hold them, so the figure is an HBM figure.  Prints one
+JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto|valu|mfma]
 
@@ -28,20 +30,20 @@ if ROOT not in sys.path:
 METRIC = "NA2D fwd queries/s and achieved HBM GB/s (% roofline), NAT-Tiny stage1 k=7"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
-KERNEL_SOURCES = {1: "na2d_valu.hip", 2: "na2d_mfma.hip"}
+KERNEL_SOURCES = {1: "na_valu.hip", 2: "na2d_mfma.hip"}
 
 
 def algorithmic_bytes(w) -> int:
     """Bytes the op itself must move: read q, k, v once, write fp32 out once,
-    read the bias table once per head (halo re-reads are not counted)."""
+    read the bias table once (halo re-reads are not counted)."""
     es = 4 if w.dtype == "f32" else 2
     per_query = 3 * w.d * es + 4 * w.d
-    return w.queries * per_query + w.heads * (2 * w.k - 1) ** 2 * 4
+    return w.queries * per_query + 4 * math.prod(w.rpb_shape)
 
 
 def algorithmic_flops(w) -> int:
-    """QK and AV: 2 * k^2 * d multiply-adds per query, a multiply-add = 2 flops."""
-    return w.queries * 4 * w.k * w.k * w.d
+    """QK and AV: 2 * keys * d multiply-adds per query, a multiply-add = 2 flops."""
+    return w.queries * 4 * w.keys_per_query * w.d
 
 
 def source_digest(name: str) -> str:
@@ -84,17 +86,26 @@ def cpu_baseline(w, x, seconds: float = 10.0):
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit() and int(env) > 0:
         cores = min(cores, int(env))
+    if w.op == "na2d":
+        def run(idx):
+            oracle.na2d_forward_sampled(x.q64, x.k64, x.v64, x.rpb64, w.k, idx, nthreads=cores)
+    else:
+        ref = {"na1d": oracle.na1d_forward, "na3d": oracle.na3d_forward,
+               "sasa2d": oracle.sasa2d_forward}[w.op]
+
+        def run(idx):
+            ref(x.q64, x.k64, x.v64, x.rpb64, w.k, idx=idx, nthreads=cores)
     rng = np.random.default_rng(1)
     probe = rng.choice(w.queries, size=min(w.queries, 4096), replace=False)
     t0 = time.perf_counter()
-    oracle.na2d_forward_sampled(x.q64, x.k64, x.v64, x.rpb64, w.k, probe, nthreads=cores)
+    run(probe)
     rate = probe.size / max(time.perf_counter() - t0, 1e-6)
     n = int(min(w.queries, max(probe.size, rate * seconds)))
     sample = rng.choice(w.queries, size=n, replace=False)
     t0 = time.perf_counter()
     done = 0
     while True:
-        oracle.na2d_forward_sampled(x.q64, x.k64, x.v64, x.rpb64, w.k, sample, nthreads=cores)
+        run(sample)
         done += n
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -147,8 +158,13 @@ def main():
     dtype_code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
     algo = ALGOS[args.algo]
     if algo == 0:
-        algo = na2d.na2d_select_algo(w.H, w.W, w.d, w.k, dtype_code)
+        # the matrix-core kernel serves the square 2D NA window only
+        algo = na2d.na2d_select_algo(w.H, w.W, w.d, w.k, dtype_code) if w.op == "na2d" else 1
     algo_name = {1: "valu", 2: "mfma"}[algo]
+    # the grid and window of the general entry point: [B, heads, D, H, W], (kd, kh, kw)
+    grid = (w.depth, w.H, w.W)
+    window = {"na1d": (1, 1, w.k), "na3d": (w.k, w.k, w.k)}.get(w.op, (1, w.k, w.k))
+    mode = na2d.NA_WINDOW_SASA if w.op == "sasa2d" else na2d.NA_WINDOW_NA
 
     x = workload_inputs(w, seed=0)
     set_bytes = algorithmic_bytes(w)
@@ -164,11 +180,16 @@ def main():
 
     def launch(i):
         q, k, v, out = sets[i % nsets]
-        st = lib.na2d_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
-                                 out.data_ptr(), w.B, w.heads, w.H, w.W, w.d, w.k, dtype_code,
-                                 algo, sptr)
+        if w.op == "na2d":
+            st = lib.na2d_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
+                                     out.data_ptr(), w.B, w.heads, w.H, w.W, w.d, w.k, dtype_code,
+                                     algo, sptr)
+        else:
+            st = lib.na_forward_nd(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
+                                   out.data_ptr(), w.B, w.heads, *grid, w.d, *window, mode,
+                                   dtype_code, algo, sptr)
         if st != 0:
-            raise RuntimeError("na2d_forward_ex failed: %s" % na2d.na2d_strerror(st))
+            raise RuntimeError("forward failed: %s" % na2d.na2d_strerror(st))
 
     for i in range(args.warmup):
         launch(i)
@@ -201,7 +222,8 @@ def main():
                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else int(traffic)}
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if wname == BENCH_WORKLOAD else
+        "%s fwd queries/s and achieved HBM GB/s (%% roofline), %s" % (w.op.upper(), wname),
         "value": round(value, 1),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -213,8 +235,9 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: Q,K,V ~ N(0,1), RPB ~ N(0,0.02), seed 0",
-        "config": {"workload": wname, "B": w.B, "heads": w.heads, "H": w.H, "W": w.W, "d": w.d,
-                   "k": w.k, "kernel": algo_name, "rotating_sets": nsets,
+        "config": {"workload": wname, "op": w.op, "B": w.B, "heads": w.heads, "D": w.depth,
+                   "H": w.H, "W": w.W, "d": w.d, "k": w.k, "kernel": algo_name,
+                   "rotating_sets": nsets,
                    "footprint_bytes": nsets * set_bytes, "algorithmic_bytes_per_step": set_bytes,
                    "hot_ms_per_step": None if hot_ms is None else round(hot_ms, 6),
                    "useful_tflops": round(tflops, 2)},

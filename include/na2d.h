@@ -60,6 +60,16 @@ typedef enum {
     NA2D_ALGO_MFMA = 2  /* query tile x key/value halo in LDS, matrix cores      */
 } na2d_algo;
 
+/* Window modes of na_forward_nd. */
+typedef enum {
+    NA_WINDOW_NA = 0,  /* Neighborhood Attention: the k nearest positions per axis, the
+                          window clamped inside the grid (start clamp(i - k/2, 0, L - k)) */
+    NA_WINDOW_SASA = 1 /* SASA: the window centred on the query (start i - k/2) over the
+                          input zero-padded by k/2: a position outside the grid is a zero
+                          key and a zero value, so its logit is bias / sqrt(d) and it
+                          takes part in the softmax but adds nothing to the output */
+} na_window;
+
 /* Status codes (0 = success). */
 enum {
     NA2D_OK = 0,
@@ -100,6 +110,55 @@ int na2d_check_args(const void *q, const void *k, const void *v, const float *rp
 /* The kernel family AUTO resolves to for these sizes (NA2D_ALGO_VALU or
  * NA2D_ALGO_MFMA), or a negative status if the sizes are invalid. */
 int na2d_select_algo(int H, int W, int d, int ksize, int dtype);
+
+/* ------------------------------------------------------------------------
+ * Neighborhood Attention over one, two or three axes, and SASA windows.
+ *
+ * The same Eq. 2-4 on a [B, heads, D, H, W] grid of queries (2D: D = 1;
+ * 1D: D = H = 1), with a kd x kh x kw window per query.  NATTEN handles 1D
+ * and 2D data (CSDN page, section 3.2) and later 1D to 3D (qiita article,
+ * section "NATTEN").  SASA is NA run on an input zero-padded by k/2 (CSDN
+ * page, section 3.1 after Eq. 4, and section 3.2); mode NA_WINDOW_SASA
+ * computes exactly that without materialising the padding.
+ *
+ *  - q, k, v, out: [B, heads, D, H, W, d] contiguous, d fastest; out float32.
+ *  - rpb: float32 [heads, 2kd-1, 2kh-1, 2kw-1], indexed on every axis by key
+ *    position minus query position plus (window - 1); NULL = no bias.
+ *  - Windows are odd and >= 1.  NA_WINDOW_NA needs each window <= its axis
+ *    length (NA2D_ERR_KSIZE otherwise); SASA windows may exceed the axis.
+ *    Windows are at most NA2D_VALU_MAX_KSIZE per axis.
+ *  - The other conventions (alignment, aliasing, ownership, streams, errors)
+ *    are those of na2d_forward.  A call with D = 1, kd = 1, kh = kw and mode
+ *    NA_WINDOW_NA is na2d_forward_ex.
+ * ------------------------------------------------------------------------ */
+
+/* General form.  `mode` is an na_window, `algo` an na2d_algo (the MFMA kernel
+ * serves the 2D NA case only; AUTO picks it where na2d_forward would). */
+int na_forward_nd(const void *q, const void *k, const void *v, const float *rpb, float *out,
+                  int B, int heads, int D, int H, int W, int d, int kd, int kh, int kw,
+                  int mode, int dtype, int algo, void *stream);
+
+/* Host-only check of na_forward_nd's arguments (no HIP call). */
+int na_check_args_nd(const void *q, const void *k, const void *v, const float *rpb,
+                     const float *out, int B, int heads, int D, int H, int W, int d, int kd,
+                     int kh, int kw, int mode, int dtype, int algo);
+
+/* NA1D over a sequence: q, k, v, out [B, heads, L, d]; rpb [heads, 2k-1]
+ * indexed by key minus query plus k-1; window start clamp(i - k/2, 0, L - k). */
+int na1d_forward(const void *q, const void *k, const void *v, const float *rpb, float *out,
+                 int B, int heads, int L, int d, int ksize, int dtype, void *stream);
+
+/* NA3D over a volume: q, k, v, out [B, heads, D, H, W, d]; rpb
+ * [heads, 2k-1, 2k-1, 2k-1] (depth, row, column offsets); a k x k x k window
+ * clamped per axis. */
+int na3d_forward(const void *q, const void *k, const void *v, const float *rpb, float *out,
+                 int B, int heads, int D, int H, int W, int d, int ksize, int dtype,
+                 void *stream);
+
+/* SASA on a 2D map: na2d_forward's layouts, but the k x k window is centred
+ * on the query over the zero-padded input (mode NA_WINDOW_SASA). */
+int sasa2d_forward(const void *q, const void *k, const void *v, const float *rpb, float *out,
+                   int B, int heads, int H, int W, int d, int ksize, int dtype, void *stream);
 
 /* Static text for a status code. */
 const char *na2d_strerror(int status);

@@ -20,7 +20,24 @@ GOOD = dict(B=2, heads=2, H=14, W=15, d=32, ksize=7)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(na2d_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:na|na1d|na2d|na3d|sasa2d)_[a-z_0-9]+)\s*\(", text)))
+
+
+def declared_arity():
+    """Parameter count of every prototype in the header."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b((?:na|na1d|na2d|na3d|sasa2d)_[a-z_0-9]+)\s*\(([^)]*)\)",
+                                    text):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_header():
+    lib = na2d.load()
+    for name, n in declared_arity().items():
+        assert len(getattr(lib, name).argtypes) == n, name
 
 
 def test_exports_every_declared_function():
@@ -129,3 +146,41 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(na2d, "LIBRARY", str(tmp_path / "libna2d.so"))
     with pytest.raises(ImportError):
         na2d.load()
+
+
+def check_nd(B=2, heads=2, D=5, H=6, W=7, d=32, kd=3, kh=3, kw=5, mode=0, dtype=na2d.NA2D_F16,
+             algo=0, q=Q, k=K, v=V, rpb=RPB, out=OUT):
+    return na2d.na_check_args_nd(q, k, v, rpb, out, B, heads, D, H, W, d, kd, kh, kw, mode, dtype,
+                                 algo)
+
+
+def test_nd_valid():
+    assert check_nd() == na2d.NA2D_OK                                     # 3D, rectangular
+    assert check_nd(D=1, H=1, W=40, kd=1, kh=1, kw=9) == na2d.NA2D_OK     # 1D
+    assert check_nd(D=1, kd=1, kh=7, kw=9, mode=1) == na2d.NA2D_OK        # SASA wider than the map
+    assert check_nd(dtype=na2d.NA2D_F32, d=128) == na2d.NA2D_OK
+
+
+def test_nd_errors():
+    assert check_nd(mode=2) == na2d.NA2D_ERR_UNSUPPORTED
+    assert check_nd(kd=7) == na2d.NA2D_ERR_KSIZE          # NA window longer than its axis
+    assert check_nd(kw=4) == na2d.NA2D_ERR_KSIZE          # even
+    assert check_nd(kh=4, mode=1) == na2d.NA2D_ERR_KSIZE  # even SASA window
+    assert check_nd(kh=0, mode=1) == na2d.NA2D_ERR_KSIZE
+    assert check_nd(D=0) == na2d.NA2D_ERR_SHAPE
+    assert check_nd(kw=65, mode=1) == na2d.NA2D_ERR_UNSUPPORTED
+    assert check_nd(algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED      # 3D: VALU only
+    assert check_nd(D=1, kd=1, kh=5, kw=5, mode=1,
+                    algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED         # SASA: VALU only
+    assert check_nd(D=1, kd=1, kh=5, kw=5, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_OK
+    n = 2 * 2 * 5 * 6 * 7 * 32
+    assert check_nd(out=Q + 16 * ((n * 2) // 16 - 1)) == na2d.NA2D_ERR_ALIAS
+    assert check_nd(rpb=RPB + 4) == na2d.NA2D_ERR_ALIGN
+
+
+def test_nd_wrappers_reject_before_launch():
+    f16 = na2d.NA2D_F16
+    assert na2d.na1d_forward(Q, K, V, RPB, OUT, 2, 2, 30, 32, 31, f16, None) == na2d.NA2D_ERR_KSIZE
+    assert na2d.na3d_forward(Q, K, V, RPB, OUT, 2, 2, 4, 9, 9, 32, 5, f16, None) == na2d.NA2D_ERR_KSIZE
+    assert na2d.sasa2d_forward(Q, K, V, RPB, OUT, 2, 2, 9, 9, 32, 6, f16, None) == na2d.NA2D_ERR_KSIZE
+    assert na2d.sasa2d_forward(Q, K, V, RPB, Q, 2, 2, 9, 9, 32, 5, f16, None) == na2d.NA2D_ERR_ALIAS

@@ -20,9 +20,9 @@ TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
 
 
 def sampled_indices(w, n_random, seed):
-    """Flat [B, heads, H, W] query indices: the last map entirely, then
-    n_random distinct random queries."""
-    per_map = w.H * w.W
+    """Flat [B, heads, (depth,) H, W] query indices: the last map entirely,
+    then n_random distinct random queries."""
+    per_map = w.depth * w.H * w.W
     last = np.arange(w.queries - per_map, w.queries, dtype=np.int64)
     rng = np.random.default_rng(seed)
     rand = rng.choice(w.queries - per_map, size=min(n_random, w.queries - per_map), replace=False)
@@ -35,14 +35,21 @@ def test_full_size_sampled(name):
     print("workload", name, flush=True)
     x = workload_inputs(w, seed=0)
     dev = torch.device("cuda")
-    out = na2d.forward(x.q.to(dev), x.k.to(dev), x.v.to(dev), x.rpb.to(dev), w.k)
+    fwd = {"na2d": na2d.forward, "na1d": na2d.forward_1d, "na3d": na2d.forward_3d,
+           "sasa2d": na2d.forward_sasa2d}[w.op]
+    out = fwd(x.q.to(dev), x.k.to(dev), x.v.to(dev), x.rpb.to(dev), w.k)
     torch.cuda.synchronize()
     got = out.cpu().double().numpy().reshape(-1, w.d)
     # properties of every output: finite, and a convex combination of values
     assert np.isfinite(got).all()
     assert np.abs(got).max() <= np.abs(x.v64).max() + TOL[w.dtype]
     idx = sampled_indices(w, 4096, seed=1)
-    want = oracle.na2d_forward_sampled(x.q64, x.k64, x.v64, x.rpb64, w.k, idx)
+    if w.op == "na2d":
+        want = oracle.na2d_forward_sampled(x.q64, x.k64, x.v64, x.rpb64, w.k, idx)
+    else:
+        ref = {"na1d": oracle.na1d_forward, "na3d": oracle.na3d_forward,
+               "sasa2d": oracle.sasa2d_forward}[w.op]
+        want = ref(x.q64, x.k64, x.v64, x.rpb64, w.k, idx=idx)
     err = np.abs(got[idx] - want).max()
     print("  max|err| %.3g over %d sampled queries" % (err, idx.size), flush=True)
     assert err <= TOL[w.dtype], "%s: max|err| %.3g > %.3g" % (name, err, TOL[w.dtype])

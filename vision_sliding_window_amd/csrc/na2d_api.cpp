@@ -13,7 +13,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0
 
 int elem_size(int dtype) { return dtype == NA2D_F32 ? 4 : 2; }
 
@@ -24,34 +24,102 @@ bool overlaps(const void *a, uint64_t abytes, const void *b, uint64_t bbytes)
     return pa < pb + bbytes && pb < pa + abytes;
 }
 
-bool valu_supports(int d, int ksize) {
-    return (d == 16 || d == 32 || d == 64 || d == 128) && ksize <= NA2D_VALU_MAX_KSIZE;
+// A grid of queries [B, heads, D, H, W] with a kd x kh x kw window.
+struct Nd {
+    int B, heads, D, H, W, d, kd, kh, kw, mode;
+    bool is_2d_na() const { return D == 1 && kd == 1 && kh == kw && mode == NA_WINDOW_NA; }
+};
+
+bool valu_supports(const Nd &n)
+{
+    return (n.d == 16 || n.d == 32 || n.d == 64 || n.d == 128) && n.kd <= NA2D_VALU_MAX_KSIZE &&
+           n.kh <= NA2D_VALU_MAX_KSIZE && n.kw <= NA2D_VALU_MAX_KSIZE;
 }
 
-// The MFMA kernel addresses one (b, h) map with 32-bit byte offsets.
-bool mfma_supports(int H, int W, int d, int ksize, int dtype) {
-    return (dtype == NA2D_F16 || dtype == NA2D_BF16) && d == 32 && ksize >= 3 &&
-           ksize <= NA2D_MFMA_MAX_KSIZE && (uint64_t)H * W * d * 4 <= 0x7fffffffull;
+// The MFMA kernel: square 2D NA windows, 16-bit inputs, d = 32; it addresses
+// one (b, h) map with 32-bit byte offsets.
+bool mfma_supports(const Nd &n, int dtype)
+{
+    return n.is_2d_na() && (dtype == NA2D_F16 || dtype == NA2D_BF16) && n.d == 32 &&
+           n.kh >= 3 && n.kh <= NA2D_MFMA_MAX_KSIZE &&
+           (uint64_t)n.H * n.W * n.d * 4 <= 0x7fffffffull;
+}
+
+bool window_ok(int k, int L, int mode)
+{
+    return k >= 1 && (k % 2) == 1 && (mode == NA_WINDOW_SASA || k <= L);
 }
 
 // Size checks shared by every entry point.
-int check_sizes(int B, int heads, int H, int W, int d, int ksize)
+int check_sizes(const Nd &n)
 {
-    if (B <= 0 || heads <= 0 || H <= 0 || W <= 0 || d <= 0) return NA2D_ERR_SHAPE;
-    const uint64_t pixels = (uint64_t)B * heads * H * W;
+    if (n.B <= 0 || n.heads <= 0 || n.D <= 0 || n.H <= 0 || n.W <= 0 || n.d <= 0)
+        return NA2D_ERR_SHAPE;
+    const uint64_t queries = (uint64_t)n.B * n.heads * n.D * n.H * n.W;
     // element counts are 64-bit inside the kernels; keep the query count within
     // what a one-dimensional grid of 256-lane workgroups can cover
-    if (pixels > (uint64_t)0x7fffffff * 64ull || pixels * (uint64_t)d > (1ull << 60))
+    if (queries > (uint64_t)0x7fffffff * 64ull || queries * (uint64_t)n.d > (1ull << 60))
         return NA2D_ERR_SHAPE;
-    if (ksize < 1 || (ksize % 2) == 0 || ksize > H || ksize > W) return NA2D_ERR_KSIZE;
+    if (!window_ok(n.kd, n.D, n.mode) || !window_ok(n.kh, n.H, n.mode) ||
+        !window_ok(n.kw, n.W, n.mode))
+        return NA2D_ERR_KSIZE;
     return NA2D_OK;
 }
 
-int resolve_algo(int H, int W, int d, int ksize, int dtype, int algo)
+int resolve_algo(const Nd &n, int dtype, int algo)
 {
     if (algo == NA2D_ALGO_AUTO)
-        return mfma_supports(H, W, d, ksize, dtype) ? NA2D_ALGO_MFMA : NA2D_ALGO_VALU;
+        return mfma_supports(n, dtype) ? NA2D_ALGO_MFMA : NA2D_ALGO_VALU;
     return algo;
+}
+
+int check_nd(const void *q, const void *k, const void *v, const float *rpb, const float *out,
+             const Nd &n, int dtype, int algo)
+{
+    if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
+    if (algo != NA2D_ALGO_AUTO && algo != NA2D_ALGO_VALU && algo != NA2D_ALGO_MFMA)
+        return NA2D_ERR_ALGO;
+    if (n.mode != NA_WINDOW_NA && n.mode != NA_WINDOW_SASA) return NA2D_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !out) return NA2D_ERR_NULL;
+    const int st = check_sizes(n);
+    if (st != NA2D_OK) return st;
+    const void *ptrs[5] = {q, k, v, out, rpb};
+    for (const void *p : ptrs)
+        if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return NA2D_ERR_ALIGN;
+    const uint64_t elems = (uint64_t)n.B * n.heads * n.D * n.H * n.W * n.d;
+    const uint64_t in_bytes = elems * elem_size(dtype), out_bytes = elems * 4;
+    const uint64_t rpb_bytes =
+        (uint64_t)n.heads * (2 * n.kd - 1) * (2 * n.kh - 1) * (2 * n.kw - 1) * 4;
+    if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
+        overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, rpb, rpb_bytes))
+        return NA2D_ERR_ALIAS;
+    const int a = resolve_algo(n, dtype, algo);
+    if (a == NA2D_ALGO_VALU && !valu_supports(n)) return NA2D_ERR_UNSUPPORTED;
+    if (a == NA2D_ALGO_MFMA && !mfma_supports(n, dtype)) return NA2D_ERR_UNSUPPORTED;
+    return NA2D_OK;
+}
+
+int forward_nd(const void *q, const void *k, const void *v, const float *rpb, float *out,
+               const Nd &n, int dtype, int algo, void *stream)
+{
+    const int st = check_nd(q, k, v, rpb, out, n, dtype, algo);
+    if (st != NA2D_OK) return st;
+    const na2d::Problem p{q,     k,      v,   rpb,  out,  n.B,  n.heads, n.H,
+                          n.W,   n.d,    n.kh, dtype, n.D, n.kd, n.kh,    n.kw,
+                          n.mode};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = resolve_algo(n, dtype, algo) == NA2D_ALGO_MFMA ? na2d::launch_mfma(p, s)
+                                                                        : na2d::launch_valu(p, s);
+    if (e != hipSuccess) {
+        g_last_error = hipGetErrorString(e);
+        return NA2D_ERR_HIP;
+    }
+    return NA2D_OK;
+}
+
+Nd nd_2d(int B, int heads, int H, int W, int d, int ksize, int mode)
+{
+    return Nd{B, heads, 1, H, W, d, 1, ksize, ksize, mode};
 }
 
 }  // namespace
@@ -60,34 +128,18 @@ extern "C" int na2d_check_args(const void *q, const void *k, const void *v, cons
                                const float *out, int B, int heads, int H, int W, int d,
                                int ksize, int dtype, int algo)
 {
-    if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
-    if (algo != NA2D_ALGO_AUTO && algo != NA2D_ALGO_VALU && algo != NA2D_ALGO_MFMA)
-        return NA2D_ERR_ALGO;
-    if (!q || !k || !v || !out) return NA2D_ERR_NULL;
-    int st = check_sizes(B, heads, H, W, d, ksize);
-    if (st != NA2D_OK) return st;
-    const void *ptrs[5] = {q, k, v, out, rpb};
-    for (const void *p : ptrs)
-        if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return NA2D_ERR_ALIGN;
-    const uint64_t n = (uint64_t)B * heads * H * W * d;
-    const uint64_t in_bytes = n * elem_size(dtype), out_bytes = n * 4;
-    const uint64_t rpb_bytes = (uint64_t)heads * (2 * ksize - 1) * (2 * ksize - 1) * 4;
-    if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
-        overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, rpb, rpb_bytes))
-        return NA2D_ERR_ALIAS;
-    const int a = resolve_algo(H, W, d, ksize, dtype, algo);
-    if (a == NA2D_ALGO_VALU && !valu_supports(d, ksize)) return NA2D_ERR_UNSUPPORTED;
-    if (a == NA2D_ALGO_MFMA && !mfma_supports(H, W, d, ksize, dtype)) return NA2D_ERR_UNSUPPORTED;
-    return NA2D_OK;
+    return check_nd(q, k, v, rpb, out, nd_2d(B, heads, H, W, d, ksize, NA_WINDOW_NA), dtype,
+                    algo);
 }
 
 extern "C" int na2d_select_algo(int H, int W, int d, int ksize, int dtype)
 {
     if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
-    int st = check_sizes(1, 1, H, W, d, ksize);
+    const Nd n = nd_2d(1, 1, H, W, d, ksize, NA_WINDOW_NA);
+    const int st = check_sizes(n);
     if (st != NA2D_OK) return st;
-    const int a = resolve_algo(H, W, d, ksize, dtype, NA2D_ALGO_AUTO);
-    if (a == NA2D_ALGO_VALU && !valu_supports(d, ksize)) return NA2D_ERR_UNSUPPORTED;
+    const int a = resolve_algo(n, dtype, NA2D_ALGO_AUTO);
+    if (a == NA2D_ALGO_VALU && !valu_supports(n)) return NA2D_ERR_UNSUPPORTED;
     return a;
 }
 
@@ -95,18 +147,8 @@ extern "C" int na2d_forward_ex(const void *q, const void *k, const void *v, cons
                                float *out, int B, int heads, int H, int W, int d, int ksize,
                                int dtype, int algo, void *stream)
 {
-    int st = na2d_check_args(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, algo);
-    if (st != NA2D_OK) return st;
-    const na2d::Problem p{q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype};
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = resolve_algo(H, W, d, ksize, dtype, algo) == NA2D_ALGO_MFMA
-                             ? na2d::launch_mfma(p, s)
-                             : na2d::launch_valu(p, s);
-    if (e != hipSuccess) {
-        g_last_error = hipGetErrorString(e);
-        return NA2D_ERR_HIP;
-    }
-    return NA2D_OK;
+    return forward_nd(q, k, v, rpb, out, nd_2d(B, heads, H, W, d, ksize, NA_WINDOW_NA), dtype,
+                      algo, stream);
 }
 
 extern "C" int na2d_forward(const void *q, const void *k, const void *v, const float *rpb,
@@ -117,15 +159,56 @@ extern "C" int na2d_forward(const void *q, const void *k, const void *v, const f
                            stream);
 }
 
+extern "C" int na_check_args_nd(const void *q, const void *k, const void *v, const float *rpb,
+                                const float *out, int B, int heads, int D, int H, int W, int d,
+                                int kd, int kh, int kw, int mode, int dtype, int algo)
+{
+    return check_nd(q, k, v, rpb, out, Nd{B, heads, D, H, W, d, kd, kh, kw, mode}, dtype, algo);
+}
+
+extern "C" int na_forward_nd(const void *q, const void *k, const void *v, const float *rpb,
+                             float *out, int B, int heads, int D, int H, int W, int d, int kd,
+                             int kh, int kw, int mode, int dtype, int algo, void *stream)
+{
+    return forward_nd(q, k, v, rpb, out, Nd{B, heads, D, H, W, d, kd, kh, kw, mode}, dtype, algo,
+                      stream);
+}
+
+extern "C" int na1d_forward(const void *q, const void *k, const void *v, const float *rpb,
+                            float *out, int B, int heads, int L, int d, int ksize, int dtype,
+                            void *stream)
+{
+    return forward_nd(q, k, v, rpb, out, Nd{B, heads, 1, 1, L, d, 1, 1, ksize, NA_WINDOW_NA},
+                      dtype, NA2D_ALGO_AUTO, stream);
+}
+
+extern "C" int na3d_forward(const void *q, const void *k, const void *v, const float *rpb,
+                            float *out, int B, int heads, int D, int H, int W, int d, int ksize,
+                            int dtype, void *stream)
+{
+    return forward_nd(q, k, v, rpb, out,
+                      Nd{B, heads, D, H, W, d, ksize, ksize, ksize, NA_WINDOW_NA}, dtype,
+                      NA2D_ALGO_AUTO, stream);
+}
+
+extern "C" int sasa2d_forward(const void *q, const void *k, const void *v, const float *rpb,
+                              float *out, int B, int heads, int H, int W, int d, int ksize,
+                              int dtype, void *stream)
+{
+    return forward_nd(q, k, v, rpb, out, nd_2d(B, heads, H, W, d, ksize, NA_WINDOW_SASA), dtype,
+                      NA2D_ALGO_AUTO, stream);
+}
+
 extern "C" const char *na2d_strerror(int status)
 {
     switch (status) {
     case NA2D_OK: return "success";
     case NA2D_ERR_NULL: return "q, k, v or out is NULL";
-    case NA2D_ERR_SHAPE: return "B, heads, H, W or d is not positive, or the problem is too large";
-    case NA2D_ERR_KSIZE: return "ksize must be odd, >= 1 and <= min(H, W)";
+    case NA2D_ERR_SHAPE: return "a size is not positive, or the problem is too large";
+    case NA2D_ERR_KSIZE: return "a window must be odd, >= 1 and (NA) no longer than its axis";
     case NA2D_ERR_DTYPE: return "dtype must be NA2D_F32, NA2D_F16 or NA2D_BF16";
-    case NA2D_ERR_UNSUPPORTED: return "head dim or ksize not supported by the selected kernel";
+    case NA2D_ERR_UNSUPPORTED:
+        return "head dim, window or mode not supported by the selected kernel";
     case NA2D_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case NA2D_ERR_ALIAS: return "out overlaps q, k, v or rpb";
     case NA2D_ERR_HIP: return "HIP runtime error (see na2d_last_error)";

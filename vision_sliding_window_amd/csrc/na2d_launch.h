@@ -5,12 +5,16 @@
 
 namespace na2d {
 
-// One validated forward problem (see include/na2d.h for the meaning of each field).
+// One validated forward problem (see include/na2d.h for the meaning of each
+// field).  The grid is [B, heads, depth, H, W] with a kd x kh x kw window;
+// `ksize` is the square window of the 2D case (kh = kw) that the MFMA kernel
+// serves.
 struct Problem {
     const void *q, *k, *v;
     const float *rpb;  // may be null: no positional bias
     float *out;
     int B, heads, H, W, d, ksize, dtype;
+    int depth, kd, kh, kw, mode;
 };
 
 // Launchers; each returns the HIP status of its launch.  The arguments have

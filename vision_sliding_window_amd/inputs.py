@@ -31,6 +31,10 @@ DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
+    """One benchmark / parity configuration.  `op` is the operation: "na2d"
+    (the default), "na1d" (a sequence of length W: H = depth = 1), "na3d" (a
+    depth x H x W volume, cubic window) or "sasa2d" (centred windows over a
+    zero-padded map)."""
     name: str
     B: int
     heads: int
@@ -39,14 +43,33 @@ class Workload:
     d: int
     k: int
     dtype: str
+    op: str = "na2d"
+    depth: int = 1
 
     @property
     def queries(self) -> int:
-        return self.B * self.heads * self.H * self.W
+        return self.B * self.heads * self.depth * self.H * self.W
 
     @property
     def shape(self):
+        if self.op == "na1d":
+            return (self.B, self.heads, self.W, self.d)
+        if self.op == "na3d":
+            return (self.B, self.heads, self.depth, self.H, self.W, self.d)
         return (self.B, self.heads, self.H, self.W, self.d)
+
+    @property
+    def rpb_shape(self):
+        return rpb_shape(self.op, self.heads, self.k)
+
+    @property
+    def keys_per_query(self) -> int:
+        return self.k ** {"na1d": 1, "na2d": 2, "sasa2d": 2, "na3d": 3}[self.op]
+
+
+def rpb_shape(op: str, heads: int, k: int):
+    n = 2 * k - 1
+    return {"na1d": (heads, n), "na3d": (heads, n, n, n)}.get(op, (heads, n, n))
 
 
 # The five workloads (tiny parity case, NAT-Tiny stage 1, all four NAT-Tiny
@@ -62,6 +85,13 @@ WORKLOADS = {
     "hires_448_f16": Workload("hires_448_f16", 1, 4, 448, 448, 32, 7, "f16"),
     "large_kernel_k13_bf16": Workload("large_kernel_k13_bf16", 8, 4, 128, 128, 32, 13, "bf16"),
     "large_kernel_k21_bf16": Workload("large_kernel_k21_bf16", 8, 4, 128, 128, 32, 21, "bf16"),
+    # beyond the 2D forward: a sequence with the same queries and keys per query
+    # as NAT-Tiny stage 1 (56 x 56 = 3136 positions, 49 keys), SASA windows on
+    # the stage-1 map, and a 16 x 56 x 56 volume with 5 x 5 x 5 windows
+    "na1d_L3136_k49_f16": Workload("na1d_L3136_k49_f16", 32, 2, 1, 3136, 32, 49, "f16", "na1d"),
+    "sasa2d_stage1_f16": Workload("sasa2d_stage1_f16", 32, 2, 56, 56, 32, 7, "f16", "sasa2d"),
+    "na3d_16x56x56_k5_f16": Workload("na3d_16x56x56_k5_f16", 2, 2, 56, 56, 32, 5, "f16", "na3d",
+                                     16),
 }
 
 BENCH_WORKLOAD = "nat_tiny_stage1_f16"
@@ -85,14 +115,15 @@ def _round(a: np.ndarray, dtype: str):
 
 
 def make_inputs(shape, ksize: int, dtype: str, seed: int = 0, rpb_std: float = 0.02,
-                q_scale: float = 1.0) -> Inputs:
-    """Draw Q, K, V ~ N(0, 1) (Q optionally times q_scale) and RPB ~ N(0, rpb_std)."""
-    B, heads, H, W, d = shape
+                q_scale: float = 1.0, op: str = "na2d") -> Inputs:
+    """Draw Q, K, V ~ N(0, 1) (Q optionally times q_scale) and RPB ~ N(0, rpb_std).
+    `shape` is [B, heads, ..., d]; the bias table is [heads, 2k-1] per axis of `op`."""
+    heads = shape[1]
     rng = np.random.default_rng(seed)
     q = rng.standard_normal(shape)
     k = rng.standard_normal(shape)
     v = rng.standard_normal(shape)
-    rpb = rng.standard_normal((heads, 2 * ksize - 1, 2 * ksize - 1)) * rpb_std
+    rpb = rng.standard_normal(rpb_shape(op, heads, ksize)) * rpb_std
     if q_scale != 1.0:
         q = q * q_scale
     qt, q64 = _round(q, dtype)
@@ -103,4 +134,4 @@ def make_inputs(shape, ksize: int, dtype: str, seed: int = 0, rpb_std: float = 0
 
 
 def workload_inputs(w: Workload, seed: int = 0, **kw) -> Inputs:
-    return make_inputs(w.shape, w.k, w.dtype, seed=seed, **kw)
+    return make_inputs(w.shape, w.k, w.dtype, seed=seed, op=w.op, **kw)

@@ -18,6 +18,7 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libna2d.so")
 
 NA2D_F32, NA2D_F16, NA2D_BF16 = 0, 1, 2
 NA2D_ALGO_AUTO, NA2D_ALGO_VALU, NA2D_ALGO_MFMA = 0, 1, 2
+NA_WINDOW_NA, NA_WINDOW_SASA = 0, 1
 NA2D_OK = 0
 NA2D_ERR_NULL = -1
 NA2D_ERR_SHAPE = -2
@@ -30,7 +31,8 @@ NA2D_ERR_HIP = -8
 NA2D_ERR_ALGO = -9
 
 EXPORTS = ["na2d_forward", "na2d_forward_ex", "na2d_check_args", "na2d_select_algo",
-           "na2d_strerror", "na2d_last_error", "na2d_version"]
+           "na2d_strerror", "na2d_last_error", "na2d_version", "na_forward_nd",
+           "na_check_args_nd", "na1d_forward", "na3d_forward", "sasa2d_forward"]
 
 TORCH_DTYPE_CODE = {torch.float32: NA2D_F32, torch.float16: NA2D_F16, torch.bfloat16: NA2D_BF16}
 
@@ -69,6 +71,16 @@ def load() -> ctypes.CDLL:
         lib.na2d_last_error.restype = ctypes.c_char_p
         lib.na2d_version.argtypes = []
         lib.na2d_version.restype = I
+        lib.na_forward_nd.argtypes = [P, P, P, P, P] + [I] * 12 + [P]
+        lib.na_forward_nd.restype = I
+        lib.na_check_args_nd.argtypes = [P, P, P, P, P] + [I] * 12
+        lib.na_check_args_nd.restype = I
+        lib.na1d_forward.argtypes = [P, P, P, P, P] + [I] * 6 + [P]
+        lib.na1d_forward.restype = I
+        lib.na3d_forward.argtypes = [P, P, P, P, P] + [I] * 8 + [P]
+        lib.na3d_forward.restype = I
+        lib.sasa2d_forward.argtypes = [P, P, P, P, P] + [I] * 7 + [P]
+        lib.sasa2d_forward.restype = I
         _lib = lib
     return _lib
 
@@ -109,6 +121,33 @@ def na2d_select_algo(H, W, d, ksize, dtype) -> int:
     return load().na2d_select_algo(H, W, d, ksize, dtype)
 
 
+def na_forward_nd(q, k, v, rpb, out, B, heads, D, H, W, d, kd, kh, kw, mode, dtype, algo,
+                  stream=None) -> int:
+    return load().na_forward_nd(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out), B, heads,
+                                D, H, W, d, kd, kh, kw, mode, dtype, algo, _stream(stream))
+
+
+def na_check_args_nd(q, k, v, rpb, out, B, heads, D, H, W, d, kd, kh, kw, mode, dtype,
+                     algo) -> int:
+    return load().na_check_args_nd(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out), B,
+                                   heads, D, H, W, d, kd, kh, kw, mode, dtype, algo)
+
+
+def na1d_forward(q, k, v, rpb, out, B, heads, L, d, ksize, dtype, stream=None) -> int:
+    return load().na1d_forward(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out), B, heads,
+                               L, d, ksize, dtype, _stream(stream))
+
+
+def na3d_forward(q, k, v, rpb, out, B, heads, D, H, W, d, ksize, dtype, stream=None) -> int:
+    return load().na3d_forward(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out), B, heads,
+                               D, H, W, d, ksize, dtype, _stream(stream))
+
+
+def sasa2d_forward(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, stream=None) -> int:
+    return load().sasa2d_forward(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out), B, heads,
+                                 H, W, d, ksize, dtype, _stream(stream))
+
+
 def na2d_strerror(status: int) -> str:
     return load().na2d_strerror(status).decode()
 
@@ -145,6 +184,74 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rpb, ksize: int,
         stream = torch.cuda.current_stream(q.device)
     st = na2d_forward_ex(q, k, v, rpb, out, B, heads, H, W, d, ksize, TORCH_DTYPE_CODE[q.dtype],
                          algo, stream)
+    if st != NA2D_OK:
+        raise NA2DError(st, na2d_last_error() if st == NA2D_ERR_HIP else "")
+    return out
+
+
+def _check_inputs(q, k, v, rpb, ndim, rpb_shape):
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous() and t.dim() == ndim):
+            raise ValueError("q, k, v must be contiguous %d-d GPU tensors" % ndim)
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    if q.dtype not in TORCH_DTYPE_CODE:
+        raise ValueError("unsupported dtype %s" % q.dtype)
+    if rpb is not None:
+        if not (rpb.is_cuda and rpb.is_contiguous() and rpb.dtype == torch.float32):
+            raise ValueError("rpb must be a contiguous float32 GPU tensor")
+        if tuple(rpb.shape) != tuple(rpb_shape):
+            raise ValueError("rpb must have shape %s" % (tuple(rpb_shape),))
+
+
+def _run(fn, q, out, stream, *args):
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fn(*args[:4], out, *args[4:], stream)
+    if st != NA2D_OK:
+        raise NA2DError(st, na2d_last_error() if st == NA2D_ERR_HIP else "")
+    return out
+
+
+def forward_1d(q, k, v, rpb, ksize: int, out=None, stream=None):
+    """NA1D on [B, heads, L, d] device tensors (rpb [heads, 2k-1]); returns fp32 out."""
+    _check_inputs(q, k, v, rpb, 4, (q.shape[1], 2 * ksize - 1))
+    B, heads, L, d = q.shape
+    return _run(na1d_forward, q, out, stream, q, k, v, rpb, B, heads, L, d, ksize,
+                TORCH_DTYPE_CODE[q.dtype])
+
+
+def forward_3d(q, k, v, rpb, ksize: int, out=None, stream=None):
+    """NA3D on [B, heads, D, H, W, d] device tensors (rpb [heads, 2k-1, 2k-1, 2k-1])."""
+    n = 2 * ksize - 1
+    _check_inputs(q, k, v, rpb, 6, (q.shape[1], n, n, n))
+    B, heads, D, H, W, d = q.shape
+    return _run(na3d_forward, q, out, stream, q, k, v, rpb, B, heads, D, H, W, d, ksize,
+                TORCH_DTYPE_CODE[q.dtype])
+
+
+def forward_sasa2d(q, k, v, rpb, ksize: int, out=None, stream=None):
+    """SASA (centred windows, zero padding) on [B, heads, H, W, d] device tensors."""
+    _check_inputs(q, k, v, rpb, 5, (q.shape[1], 2 * ksize - 1, 2 * ksize - 1))
+    B, heads, H, W, d = q.shape
+    return _run(sasa2d_forward, q, out, stream, q, k, v, rpb, B, heads, H, W, d, ksize,
+                TORCH_DTYPE_CODE[q.dtype])
+
+
+def forward_nd(q, k, v, rpb, window, mode=NA_WINDOW_NA, algo=NA2D_ALGO_AUTO, out=None,
+               stream=None):
+    """The general form on [B, heads, D, H, W, d] tensors with a (kd, kh, kw) window."""
+    kd, kh, kw = window
+    _check_inputs(q, k, v, rpb, 6, (q.shape[1], 2 * kd - 1, 2 * kh - 1, 2 * kw - 1))
+    B, heads, D, H, W, d = q.shape
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = na_forward_nd(q, k, v, rpb, out, B, heads, D, H, W, d, kd, kh, kw, mode,
+                       TORCH_DTYPE_CODE[q.dtype], algo, stream)
     if st != NA2D_OK:
         raise NA2DError(st, na2d_last_error() if st == NA2D_ERR_HIP else "")
     return out
