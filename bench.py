@@ -158,8 +158,9 @@ def main():
     dtype_code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
     algo = ALGOS[args.algo]
     if algo == 0:
-        # the matrix-core kernel serves the square 2D NA window only
-        algo = na2d.na2d_select_algo(w.H, w.W, w.d, w.k, dtype_code) if w.op == "na2d" else 1
+        # the matrix-core kernel serves square 2D windows (NA and SASA)
+        algo = (na2d.na2d_select_algo(w.H, w.W, w.d, w.k, dtype_code)
+                if w.op in ("na2d", "sasa2d") else na2d.NA2D_ALGO_VALU)
     algo_name = {1: "valu", 2: "mfma"}[algo]
     # the grid and window of the general entry point: [B, heads, D, H, W], (kd, kh, kw)
     grid = (w.depth, w.H, w.W)

@@ -132,8 +132,9 @@ int na2d_select_algo(int H, int W, int d, int ksize, int dtype);
  *    NA_WINDOW_NA is na2d_forward_ex.
  * ------------------------------------------------------------------------ */
 
-/* General form.  `mode` is an na_window, `algo` an na2d_algo (the MFMA kernel
- * serves the 2D NA case only; AUTO picks it where na2d_forward would). */
+/* General form.  `mode` is an na_window, `algo` an na2d_algo.  The MFMA
+ * kernel serves square 2D windows (D = 1, kd = 1, kh = kw), NA or SASA, with
+ * na2d_forward's dtype, d and ksize limits; AUTO picks it wherever it can. */
 int na_forward_nd(const void *q, const void *k, const void *v, const float *rpb, float *out,
                   int B, int heads, int D, int H, int W, int d, int kd, int kh, int kw,
                   int mode, int dtype, int algo, void *stream);

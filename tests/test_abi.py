@@ -170,8 +170,10 @@ def test_nd_errors():
     assert check_nd(D=0) == na2d.NA2D_ERR_SHAPE
     assert check_nd(kw=65, mode=1) == na2d.NA2D_ERR_UNSUPPORTED
     assert check_nd(algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED      # 3D: VALU only
-    assert check_nd(D=1, kd=1, kh=5, kw=5, mode=1,
-                    algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED         # SASA: VALU only
+    assert check_nd(D=1, kd=1, kh=5, kw=3, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED
+    assert check_nd(D=1, kd=1, kh=5, kw=5, mode=1, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_OK
+    assert check_nd(D=1, kd=1, kh=9, kw=9, H=6, W=7, mode=1,
+                    algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_OK      # SASA window wider than the map
     assert check_nd(D=1, kd=1, kh=5, kw=5, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_OK
     n = 2 * 2 * 5 * 6 * 7 * 32
     assert check_nd(out=Q + 16 * ((n * 2) // 16 - 1)) == na2d.NA2D_ERR_ALIAS

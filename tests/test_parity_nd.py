@@ -97,3 +97,27 @@ def test_general_matches_na2d():
                         dev(x.rpb).reshape(2, 1, 13, 13), (1, 7, 7), algo=na2d.NA2D_ALGO_VALU)
     torch.cuda.synchronize()
     assert torch.equal(a.reshape(sh), b)
+
+
+SASA_MFMA = [((2, 2, 13, 17, 32), 3), ((1, 2, 21, 19, 32), 7), ((1, 1, 5, 6, 32), 7),
+             ((2, 1, 20, 9, 32), 5), ((1, 2, 30, 33, 32), 9), ((1, 1, 8, 8, 32), 11),
+             ((1, 2, 29, 37, 32), 11), ((1, 1, 27, 25, 32), 13), ((1, 1, 23, 23, 32), 21),
+             ((1, 1, 10, 12, 32), 25), ((2, 2, 57, 55, 32), 7)]
+
+
+@pytest.mark.parametrize("shape,ks", SASA_MFMA, ids=str)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("algo", [na2d.NA2D_ALGO_VALU, na2d.NA2D_ALGO_MFMA])
+def test_sasa2d_both_kernels(shape, ks, dtype, algo):
+    """SASA through each kernel family: ragged maps, windows up to 25, windows
+    wider than the map (all padding past the edge)."""
+    print("sasa2d", shape, ks, dtype, algo, flush=True)
+    x = make_inputs(shape, ks, dtype, seed=6, rpb_std=1.0)
+    B, heads, H, W, d = shape
+    sh = (B, heads, 1, H, W, d)
+    got = na2d.forward_nd(dev(x.q).reshape(sh), dev(x.k).reshape(sh), dev(x.v).reshape(sh),
+                          dev(x.rpb).reshape(heads, 1, 2 * ks - 1, 2 * ks - 1), (1, ks, ks),
+                          na2d.NA_WINDOW_SASA, algo)
+    torch.cuda.synchronize()
+    finish(got.reshape(shape), oracle.sasa2d_forward(x.q64, x.k64, x.v64, x.rpb64, ks), dtype,
+           "sasa2d %s k=%d algo=%d" % (shape, ks, algo))

@@ -27,7 +27,6 @@ bool overlaps(const void *a, uint64_t abytes, const void *b, uint64_t bbytes)
 // A grid of queries [B, heads, D, H, W] with a kd x kh x kw window.
 struct Nd {
     int B, heads, D, H, W, d, kd, kh, kw, mode;
-    bool is_2d_na() const { return D == 1 && kd == 1 && kh == kw && mode == NA_WINDOW_NA; }
 };
 
 bool valu_supports(const Nd &n)
@@ -36,11 +35,12 @@ bool valu_supports(const Nd &n)
            n.kh <= NA2D_VALU_MAX_KSIZE && n.kw <= NA2D_VALU_MAX_KSIZE;
 }
 
-// The MFMA kernel: square 2D NA windows, 16-bit inputs, d = 32; it addresses
-// one (b, h) map with 32-bit byte offsets.
+// The MFMA kernel: square 2D windows (NA or SASA), 16-bit inputs, d = 32; it
+// addresses one (b, h) map with 32-bit byte offsets.
 bool mfma_supports(const Nd &n, int dtype)
 {
-    return n.is_2d_na() && (dtype == NA2D_F16 || dtype == NA2D_BF16) && n.d == 32 &&
+    return n.D == 1 && n.kd == 1 && n.kh == n.kw && (dtype == NA2D_F16 || dtype == NA2D_BF16) &&
+           n.d == 32 &&
            n.kh >= 3 && n.kh <= NA2D_MFMA_MAX_KSIZE &&
            (uint64_t)n.H * n.W * n.d * 4 <= 0x7fffffffull;
 }

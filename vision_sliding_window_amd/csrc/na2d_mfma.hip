@@ -112,12 +112,19 @@ __device__ inline void opaque(P *&p)
     asm volatile("" : "+v"(p));
 }
 
-// Start of the window of ks pixels around i on an axis of length L.
+// Start of the window of ks pixels around i on an axis of length L: for NA
+// (WM = NA_WINDOW_NA) the ks nearest pixels, pushed inward at the borders;
+// for SASA (NA_WINDOW_SASA) the window centred on i, reaching into the zero
+// padding past either end.
+template <int WM>
 __device__ inline int window_start(int i, int ks, int L)
 {
     int s = i - (ks >> 1);
-    s = s < 0 ? 0 : s;
-    return s > L - ks ? L - ks : s;
+    if constexpr (WM == NA_WINDOW_NA) {
+        s = s < 0 ? 0 : s;
+        s = s > L - ks ? L - ks : s;
+    }
+    return s;
 }
 
 struct Args {
@@ -184,7 +191,7 @@ struct Tile {
     int64_t map_base;  // first pixel of the (b, h) map
 };
 
-template <int TY, int TX, int NC>
+template <int TY, int TX, int NC, int WM>
 __device__ inline Tile tile_geometry(const Args &a, unsigned t)
 {
     // tiles are numbered head-major (head, batch, tile row, tile col), so that a
@@ -201,10 +208,18 @@ __device__ inline Tile tile_geometry(const Args &a, unsigned t)
     g.x0 = tx * TX;
     // halo rows [hy0, hy0 + hr) hold every window of the tile's rows; LDS has
     // lr >= hr rows, the ones past the map zero-filled
-    g.hr = min(TY + a.ks - 1, a.H);
-    g.hy0 = min(window_start(g.y0, a.ks, a.H), a.H - g.hr);
-    // halo cols [cx, cx + NC) hold the windows of columns x0 .. x0 + TX - 1
-    g.cx = a.W >= NC ? min(window_start(g.x0, a.ks, a.W), a.W - NC) : 0;
+    // halo cols [cx, cx + NC) hold the windows of columns x0 .. x0 + TX - 1.
+    // SASA windows are centred, so the halo is too; its rows and columns past
+    // the map are the zero padding (they load as zeros).
+    if constexpr (WM == NA_WINDOW_SASA) {
+        g.hr = TY + a.ks - 1;
+        g.hy0 = g.y0 - (a.ks >> 1);
+        g.cx = g.x0 - (a.ks >> 1);
+    } else {
+        g.hr = min(TY + a.ks - 1, a.H);
+        g.hy0 = min(window_start<WM>(g.y0, a.ks, a.H), a.H - g.hr);
+        g.cx = a.W >= NC ? min(window_start<WM>(g.x0, a.ks, a.W), a.W - NC) : 0;
+    }
     return g;
 }
 
@@ -332,8 +347,9 @@ __device__ inline void stage_tile(const Args &a, const Tile &t, unsigned char *s
             const int c = 16 * cb + c_lane;
             const int sl = slot ^ ((c >> 2) & 3);  // the d-slice this LDS slot holds
             const int gx = t.cx + c;
-            const unsigned off = gy < a.H && gx < a.W ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
-                                                      : kOutOfRange;
+            const unsigned off = (unsigned)gy < (unsigned)a.H && (unsigned)gx < (unsigned)a.W
+                                     ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
+                                     : kOutOfRange;
             unsigned char *dk = smem + (unsigned)(r * S::NC + 16 * cb) * 64u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)dk, 16, off, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dk + halo_bytes(lr, S::NC)), 16,
@@ -362,7 +378,7 @@ __device__ inline void stage_tile(const Args &a, const Tile &t, unsigned char *s
 //  kGeneral:  split layout, general table with per-row / per-column indices.
 enum { kClass = 0, kInterior = 1, kGeneral = 2 };
 
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int MODE>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int MODE, int WM>
 __device__ inline void attend(const Args &a, const Tile &t, const unsigned char *smem,
                               const float *btab, int lr, int wave, int ry, int lane,
                               const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum)
@@ -395,8 +411,8 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
     lds_cf32 *bneg = nullptr;
     int sy = 0, lo = 0, coloff[NCB][4];
     if constexpr (MODE == kClass) {
-        sy = window_start(y, ks, H);
-        const int ex = x - window_start(x, ks, W);
+        sy = window_start<WM>(y, ks, H);
+        const int ex = x - window_start<WM>(x, ks, W);
         lo = sy - ry;  // first candidate row inside the window
         const int nb = 2 * ks - 1;
         bp = (lds_cf32 *)btab + ex * (nb * PC) + (ry - y + ks - 1) * PC + (t.cx - x + ks - 1) +
@@ -406,8 +422,8 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
         bp = (lds_cf32 *)btab + 4 * ks * ks + (QY - 1 - qy) * P + (QX - 1 - qx + 4 * g);
     } else {
         bp = (lds_cf32 *)btab;
-        sy = window_start(y, ks, H);
-        const int sx = window_start(x, ks, W);
+        sy = window_start<WM>(y, ks, H);
+        const int sx = window_start<WM>(x, ks, W);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -538,7 +554,7 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 
 // One wave's share of a tile: choose its candidate key rows and the bias
 // path, leave o / lsum for store_out.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM>
 __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned char *smem,
                                    const float *btab, int lr, int wave, int lane,
                                    const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum)
@@ -547,17 +563,22 @@ __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned 
     const int ks = KS ? KS : a.ks, H = a.H, W = a.W, r = ks >> 1;
     const int nr = wave_rows(QY, RPC, ks);
     const int y1 = t.y0 + QY * wave;
-    const int ry = max(t.hy0, min(window_start(min(y1, H - 1), ks, H), t.hy0 + t.hr - nr));
+    const int ry = max(t.hy0, min(window_start<WM>(min(y1, H - 1), ks, H), t.hy0 + t.hr - nr));
     if constexpr (S::CLS) {
-        attend<T, QY, QX, NCB, RPC, KS, kClass>(a, t, smem, btab, lr, wave, ry, lane, qf, o, lsum);
+        attend<T, QY, QX, NCB, RPC, KS, kClass, WM>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
+                                                    lsum);
     } else {
-        const bool interior = y1 - r >= 0 && y1 + QY - 1 + r <= H - 1 && t.x0 - r >= 0 &&
-                              t.x0 + QX - 1 + r <= W - 1 && ry == y1 - r && t.cx == t.x0 - r;
+        // no query window clamped (SASA windows never are), and the candidate
+        // rows / columns start k/2 above / left of the subtile's first query
+        const bool unclamped = WM == NA_WINDOW_SASA ||
+                               (y1 - r >= 0 && y1 + QY - 1 + r <= H - 1 && t.x0 - r >= 0 &&
+                                t.x0 + QX - 1 + r <= W - 1);
+        const bool interior = unclamped && ry == y1 - r && t.cx == t.x0 - r;
         if (interior)
-            attend<T, QY, QX, NCB, RPC, KS, kInterior>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
+            attend<T, QY, QX, NCB, RPC, KS, kInterior, WM>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
                                                        lsum);
         else
-            attend<T, QY, QX, NCB, RPC, KS, kGeneral>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
+            attend<T, QY, QX, NCB, RPC, KS, kGeneral, WM>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
                                                       lsum);
     }
 }
@@ -591,7 +612,7 @@ __device__ inline void store_out(const Args &a, const Tile &t, int wave, int lan
 // workgroups sharing an L2 work on neighbouring tiles).  Per tile: attend,
 // barrier, issue the next tile's copies, store this tile's outputs, wait for
 // the copies only, barrier.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM>
 __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
 {
     using S = Shape<QY, QX, NCB, RPC>;
@@ -617,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
 
     float *bt = reinterpret_cast<float *>(smem + b_offset(lr, S::NC));
     FragT qf;
-    Tile t = tile_geometry<S::TY, S::TX, S::NC>(a, tile);
+    Tile t = tile_geometry<S::TY, S::TX, S::NC, WM>(a, tile);
     int bias_head = t.h;
     stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, ks, t.h, bt, reinterpret_cast<float *>(smem), nr, tid);
     stage_tile<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf);
@@ -626,12 +647,12 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
     while (true) {
         floatx4 o[2];
         float lsum;
-        attend_wave<T, QY, QX, NCB, RPC, KS>(a, t, smem, bt, lr, wave, lane, qf, o, lsum);
+        attend_wave<T, QY, QX, NCB, RPC, KS, WM>(a, t, smem, bt, lr, wave, lane, qf, o, lsum);
         const Tile done = t;
         const unsigned next = tile + step;
         __syncthreads();  // every wave is done reading the LDS copy
         if (next < end) {
-            t = tile_geometry<S::TY, S::TX, S::NC>(a, next);
+            t = tile_geometry<S::TY, S::TX, S::NC, WM>(a, next);
             if (t.h != bias_head) {  // rare: the tile list is head-major
                 stage_bias<QY, QX, S::NC, RPC, S::CLS>(a, ks, t.h, bt, reinterpret_cast<float *>(smem), nr, tid);
                 bias_head = t.h;
@@ -680,9 +701,10 @@ __device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, in
             const int c = 16 * cb + c_lane;
             const int sl = slot ^ ((c >> 2) & 3);
             const int gx = t.cx + c;
-            const unsigned off = live && r < LR && gy < a.H && gx < a.W
-                                     ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
-                                     : kOutOfRange;
+            const unsigned off =
+                live && r < LR && (unsigned)gy < (unsigned)a.H && (unsigned)gx < (unsigned)a.W
+                    ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
+                    : kOutOfRange;
             rg.k[j][cb] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
             rg.v[j][cb] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
         }
@@ -718,7 +740,7 @@ __device__ inline void write_tile_regs(unsigned char *smem, int wave, int lane,
     }
 }
 
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM>
 __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
 {
     using S = Shape<QY, QX, NCB, RPC, NW>;
@@ -749,13 +771,13 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
     // and each be waited for alone.
     constexpr int NV = raw_per_thread(KS, S::NT);
     TileRegs<QY, QX, NCB, LR, NW> rg0, rg;
-    Tile t = tile_geometry<S::TY, S::TX, S::NC>(a, tile);
+    Tile t = tile_geometry<S::TY, S::TX, S::NC, WM>(a, tile);
     int bias_head = t.h;
     float raw_bias[NV];
     load_raw_bias<S::NT>(a, KS, t.h, tid, raw_bias);
     load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, t, wave, lane, rg0);
     unsigned next = tile + step;
-    Tile tn = tile_geometry<S::TY, S::TX, S::NC>(a, next < end ? next : tile);
+    Tile tn = tile_geometry<S::TY, S::TX, S::NC, WM>(a, next < end ? next : tile);
     load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, tn, wave, lane, rg, next < end);
     // the halo area is free until the first tile is written into it
     stage_bias<QY, QX, S::NC, RPC, S::CLS, S::NT>(a, KS, raw_bias, btab,
@@ -769,7 +791,7 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
         float lsum = 1.f;
         if (t.y0 + QY * wave < a.H) {  // the bottom tile row may leave whole waves idle
             const FragT qf = __builtin_bit_cast(FragT, *qfrag);
-            attend_wave<T, QY, QX, NCB, RPC, KS>(a, t, halo, btab, LR, wave, lane, qf, o, lsum);
+            attend_wave<T, QY, QX, NCB, RPC, KS, WM>(a, t, halo, btab, LR, wave, lane, qf, o, lsum);
         }
         const Tile done = t;
         const bool more = next < end;
@@ -793,7 +815,7 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
         tile = next;
         next = tile + step;
         if (next < end) {
-            tn = tile_geometry<S::TY, S::TX, S::NC>(a, next);
+            tn = tile_geometry<S::TY, S::TX, S::NC, WM>(a, next);
             load_tile_regs<T, QY, QX, NCB, RPC, LR>(a, tn, wave, lane, rg);
         }
         __syncthreads();  // the new halo is visible
@@ -868,7 +890,7 @@ hipError_t launch_persistent(K kern, Args &a, int threads, size_t lds, hipStream
 }
 
 // General kernel sizes: the LDS-DMA kernel with 4 waves per workgroup.
-template <typename T, int QY, int QX, int NCB, int RPC>
+template <typename T, int QY, int QX, int NCB, int RPC, int WM>
 hipError_t launch_dma(const Problem &p, hipStream_t stream)
 {
     using S = Shape<QY, QX, NCB, RPC>;
@@ -877,28 +899,35 @@ hipError_t launch_dma(const Problem &p, hipStream_t stream)
     const int nr = wave_rows(QY, RPC, p.ksize);
     const size_t lds =
         lds_bytes(a.lr, S::NC, bias_floats(S::CLS, p.ksize, nr, QY, QX, S::NC, RPC));
-    return launch_persistent(na2d_mfma_kernel<T, QY, QX, NCB, RPC, 0>, a, S::NT, lds, stream);
+    return launch_persistent(na2d_mfma_kernel<T, QY, QX, NCB, RPC, 0, WM>, a, S::NT, lds, stream);
 }
 
 // A compile-time kernel size: the register-prefetch kernel with NW waves.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM>
 hipError_t launch_pipe(const Problem &p, hipStream_t stream)
 {
     using S = Shape<QY, QX, NCB, RPC, NW>;
     Args a;
     if (!make_args<S, QY, RPC>(p, a)) return hipErrorInvalidConfiguration;
-    return launch_persistent(na2d_mfma_pipe_kernel<T, QY, QX, NCB, RPC, KS, NW>, a, S::NT, 0,
+    return launch_persistent(na2d_mfma_pipe_kernel<T, QY, QX, NCB, RPC, KS, NW, WM>, a, S::NT, 0,
                              stream);
 }
 
-template <typename T>
+template <typename T, int WM>
 hipError_t launch_typed(const Problem &p, hipStream_t stream)
 {
     const int ks = p.ksize;
-    if (ks == 7) return launch_pipe<T, 2, 8, 1, 8, 7, 4>(p, stream);
-    if (ks <= 9) return launch_dma<T, 2, 8, 1, 2>(p, stream);
-    if (ks <= 13) return launch_dma<T, 4, 4, 1, 8>(p, stream);
-    return launch_dma<T, 2, 8, 2, 2>(p, stream);
+    if (ks == 7) return launch_pipe<T, 2, 8, 1, 8, 7, 4, WM>(p, stream);
+    if (ks <= 9) return launch_dma<T, 2, 8, 1, 2, WM>(p, stream);
+    if (ks <= 13) return launch_dma<T, 4, 4, 1, 8, WM>(p, stream);
+    return launch_dma<T, 2, 8, 2, 2, WM>(p, stream);
+}
+
+template <typename T>
+hipError_t launch_mode(const Problem &p, hipStream_t stream)
+{
+    return p.mode == NA_WINDOW_SASA ? launch_typed<T, NA_WINDOW_SASA>(p, stream)
+                                    : launch_typed<T, NA_WINDOW_NA>(p, stream);
 }
 
 }  // namespace
@@ -908,8 +937,9 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream)
     if (p.d != kD || p.ksize < 3 || p.ksize > NA2D_MFMA_MAX_KSIZE) return hipErrorInvalidValue;
     // byte offsets inside one map are 32-bit (buffer addressing)
     if ((uint64_t)p.H * p.W * (kD * 4) > 0x7fffffffull) return hipErrorInvalidValue;
-    if (p.dtype == NA2D_F16) return launch_typed<_Float16>(p, stream);
-    if (p.dtype == NA2D_BF16) return launch_typed<__bf16>(p, stream);
+    if (p.depth != 1 || p.kd != 1 || p.kh != p.kw) return hipErrorInvalidValue;
+    if (p.dtype == NA2D_F16) return launch_mode<_Float16>(p, stream);
+    if (p.dtype == NA2D_BF16) return launch_mode<__bf16>(p, stream);
     return hipErrorInvalidValue;
 }
 
