@@ -31,6 +31,7 @@ METRIC = "NA2D fwd queries/s and achieved HBM GB/s (% roofline), NAT-Tiny stage1
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
 KERNEL_SOURCES = {1: "na_valu.hip", 2: "na2d_mfma.hip"}
+KERNEL_SOURCES_1D = {1: "na_valu.hip", 2: "na1d_mfma.hip"}
 
 
 def algorithmic_bytes(w) -> int:
@@ -159,8 +160,12 @@ def main():
     algo = ALGOS[args.algo]
     if algo == 0:
         # the matrix-core kernel serves square 2D windows (NA and SASA)
-        algo = (na2d.na2d_select_algo(w.H, w.W, w.d, w.k, dtype_code)
-                if w.op in ("na2d", "sasa2d") else na2d.NA2D_ALGO_VALU)
+        if w.op in ("na2d", "sasa2d"):
+            algo = na2d.na2d_select_algo(w.H, w.W, w.d, w.k, dtype_code)
+        elif w.op == "na1d" and w.dtype != "f32" and w.d == 32 and 3 <= w.k <= 63:
+            algo = na2d.NA2D_ALGO_MFMA
+        else:
+            algo = na2d.NA2D_ALGO_VALU
     algo_name = {1: "valu", 2: "mfma"}[algo]
     # the grid and window of the general entry point: [B, heads, D, H, W], (kd, kh, kw)
     grid = (w.depth, w.H, w.W)
@@ -218,7 +223,8 @@ def main():
     value = w.queries / (ms * 1e-3)
     gbs = set_bytes / (ms * 1e-3) / 1e9
     tflops = algorithmic_flops(w) / (ms * 1e-3) / 1e12
-    traffic = read_traffic(wname, algo_name, KERNEL_SOURCES[algo])
+    traffic = read_traffic(wname, algo_name,
+                           (KERNEL_SOURCES_1D if w.op == "na1d" else KERNEL_SOURCES)[algo])
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else int(traffic)}

@@ -88,6 +88,8 @@ enum {
  * the VALU kernel and 32 for the MFMA kernel. */
 #define NA2D_VALU_MAX_KSIZE 63
 #define NA2D_MFMA_MAX_KSIZE 25
+/* Largest window of the NA1D matrix-core kernel (d = 32, 16-bit inputs). */
+#define NA1D_MFMA_MAX_KSIZE 63
 
 /* Fused NA2D forward (CSDN page, section 3.1, Eq. 2-4), kernel chosen
  * automatically.  Sizes are element counts; see the conventions above. */
@@ -133,8 +135,10 @@ int na2d_select_algo(int H, int W, int d, int ksize, int dtype);
  * ------------------------------------------------------------------------ */
 
 /* General form.  `mode` is an na_window, `algo` an na2d_algo.  The MFMA
- * kernel serves square 2D windows (D = 1, kd = 1, kh = kw), NA or SASA, with
- * na2d_forward's dtype, d and ksize limits; AUTO picks it wherever it can. */
+ * kernels serve 16-bit inputs with d = 32 in two shapes: square 2D windows
+ * (D = 1, kd = 1, kh = kw, 3 <= kh <= NA2D_MFMA_MAX_KSIZE), NA or SASA, and
+ * NA1D (D = H = 1, kd = kh = 1, 3 <= kw <= NA1D_MFMA_MAX_KSIZE, NA).  AUTO
+ * picks them wherever they apply. */
 int na_forward_nd(const void *q, const void *k, const void *v, const float *rpb, float *out,
                   int B, int heads, int D, int H, int W, int d, int kd, int kh, int kw,
                   int mode, int dtype, int algo, void *stream);

@@ -171,6 +171,11 @@ def test_nd_errors():
     assert check_nd(kw=65, mode=1) == na2d.NA2D_ERR_UNSUPPORTED
     assert check_nd(algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED      # 3D: VALU only
     assert check_nd(D=1, kd=1, kh=5, kw=3, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED
+    one_d = dict(D=1, H=1, W=300, kd=1, kh=1)
+    assert check_nd(kw=63, algo=na2d.NA2D_ALGO_MFMA, **one_d) == na2d.NA2D_OK       # NA1D kernel
+    assert check_nd(kw=65, algo=na2d.NA2D_ALGO_MFMA, **one_d) == na2d.NA2D_ERR_UNSUPPORTED
+    assert check_nd(kw=9, mode=1, algo=na2d.NA2D_ALGO_MFMA, **one_d) == na2d.NA2D_ERR_UNSUPPORTED
+    assert check_nd(kw=9, d=64, algo=na2d.NA2D_ALGO_MFMA, **one_d) == na2d.NA2D_ERR_UNSUPPORTED
     assert check_nd(D=1, kd=1, kh=5, kw=5, mode=1, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_OK
     assert check_nd(D=1, kd=1, kh=9, kw=9, H=6, W=7, mode=1,
                     algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_OK      # SASA window wider than the map

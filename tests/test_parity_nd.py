@@ -121,3 +121,27 @@ def test_sasa2d_both_kernels(shape, ks, dtype, algo):
     torch.cuda.synchronize()
     finish(got.reshape(shape), oracle.sasa2d_forward(x.q64, x.k64, x.v64, x.rpb64, ks), dtype,
            "sasa2d %s k=%d algo=%d" % (shape, ks, algo))
+
+
+NA1D_MFMA = [((2, 2, 37, 32), 7), ((1, 3, 100, 32), 49), ((1, 1, 9, 32), 9), ((2, 1, 64, 32), 5),
+             ((1, 2, 130, 32), 17), ((1, 2, 131, 32), 19), ((1, 1, 63, 32), 63),
+             ((2, 2, 257, 32), 63), ((1, 1, 3, 32), 3), ((3, 2, 1000, 32), 33),
+             ((1, 1, 129, 32), 51)]
+
+
+@pytest.mark.parametrize("shape,ks", NA1D_MFMA, ids=str)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("algo", [na2d.NA2D_ALGO_VALU, na2d.NA2D_ALGO_MFMA])
+def test_na1d_both_kernels(shape, ks, dtype, algo):
+    """NA1D through each kernel family: sequences shorter than, equal to and
+    ragged against the 64-query tile, windows from 3 to 63, L = k."""
+    print("na1d", shape, ks, dtype, algo, flush=True)
+    x = make_inputs(shape, ks, dtype, seed=7, rpb_std=1.0, op="na1d")
+    B, heads, L, d = shape
+    sh = (B, heads, 1, 1, L, d)
+    got = na2d.forward_nd(dev(x.q).reshape(sh), dev(x.k).reshape(sh), dev(x.v).reshape(sh),
+                          dev(x.rpb).reshape(heads, 1, 1, 2 * ks - 1), (1, 1, ks),
+                          na2d.NA_WINDOW_NA, algo)
+    torch.cuda.synchronize()
+    finish(got.reshape(shape), oracle.na1d_forward(x.q64, x.k64, x.v64, x.rpb64, ks), dtype,
+           "na1d %s k=%d algo=%d" % (shape, ks, algo))

@@ -35,14 +35,25 @@ bool valu_supports(const Nd &n)
            n.kh <= NA2D_VALU_MAX_KSIZE && n.kw <= NA2D_VALU_MAX_KSIZE;
 }
 
-// The MFMA kernel: square 2D windows (NA or SASA), 16-bit inputs, d = 32; it
-// addresses one (b, h) map with 32-bit byte offsets.
+// The NA1D matrix-core kernel: a sequence (D = H = 1) with a 1 x 1 x kw NA window.
+bool is_mfma_1d(const Nd &n)
+{
+    return n.D == 1 && n.H == 1 && n.kd == 1 && n.kh == 1 && n.mode == NA_WINDOW_NA &&
+           n.kw >= 3 && n.kw <= NA1D_MFMA_MAX_KSIZE;
+}
+
+// The 2D matrix-core kernel: square windows (NA or SASA).
+bool is_mfma_2d(const Nd &n)
+{
+    return n.D == 1 && n.kd == 1 && n.kh == n.kw && n.kh >= 3 && n.kh <= NA2D_MFMA_MAX_KSIZE;
+}
+
+// Both take 16-bit inputs with d = 32 and address one (b, h) map with 32-bit
+// byte offsets.
 bool mfma_supports(const Nd &n, int dtype)
 {
-    return n.D == 1 && n.kd == 1 && n.kh == n.kw && (dtype == NA2D_F16 || dtype == NA2D_BF16) &&
-           n.d == 32 &&
-           n.kh >= 3 && n.kh <= NA2D_MFMA_MAX_KSIZE &&
-           (uint64_t)n.H * n.W * n.d * 4 <= 0x7fffffffull;
+    return (dtype == NA2D_F16 || dtype == NA2D_BF16) && n.d == 32 &&
+           (is_mfma_1d(n) || is_mfma_2d(n)) && (uint64_t)n.H * n.W * n.d * 4 <= 0x7fffffffull;
 }
 
 bool window_ok(int k, int L, int mode)
@@ -108,8 +119,11 @@ int forward_nd(const void *q, const void *k, const void *v, const float *rpb, fl
                           n.W,   n.d,    n.kh, dtype, n.D, n.kd, n.kh,    n.kw,
                           n.mode};
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = resolve_algo(n, dtype, algo) == NA2D_ALGO_MFMA ? na2d::launch_mfma(p, s)
-                                                                        : na2d::launch_valu(p, s);
+    hipError_t e;
+    if (resolve_algo(n, dtype, algo) == NA2D_ALGO_MFMA)
+        e = is_mfma_1d(n) ? na2d::launch_mfma_1d(p, s) : na2d::launch_mfma(p, s);
+    else
+        e = na2d::launch_valu(p, s);
     if (e != hipSuccess) {
         g_last_error = hipGetErrorString(e);
         return NA2D_ERR_HIP;

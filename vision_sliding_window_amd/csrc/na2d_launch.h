@@ -20,6 +20,7 @@ struct Problem {
 // Launchers; each returns the HIP status of its launch.  The arguments have
 // been checked by the caller.
 hipError_t launch_valu(const Problem &p, hipStream_t stream);
-hipError_t launch_mfma(const Problem &p, hipStream_t stream);
+hipError_t launch_mfma(const Problem &p, hipStream_t stream);     // square 2D windows
+hipError_t launch_mfma_1d(const Problem &p, hipStream_t stream);  // NA1D
 
 }  // namespace na2d

@@ -1,0 +1,82 @@
+// na_mfma_util.h -- device helpers shared by the matrix-core kernels (gfx950):
+// fragment types, the 16x16x32 MFMA wrappers, the cross-lane reductions of
+// the S^T = K Q^T layout, and raw buffer descriptors.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace na2d {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const unsigned char lds_cu8;
+typedef __attribute__((address_space(3))) const u32x4 lds_cu4;
+typedef __attribute__((address_space(3))) const float lds_cf32;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr int kD = 32;        // head dim handled here
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+constexpr unsigned kOutOfRange = 0x7ffffff0u;  // byte offset past any map: loads 0, stores dropped
+
+template <typename T> struct Frag;
+template <> struct Frag<_Float16> { typedef half8 type; };
+template <> struct Frag<__bf16> { typedef bf16x8 type; };
+
+__device__ inline floatx4 mfma16x16x32(const half8 &a, const half8 &b, const floatx4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const floatx4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Max and sum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 that hold one query.
+// v_permlane16_swap(x, x) returns both members of each (l, l ^ 16) pair in its
+// two results (and likewise permlane32 for l ^ 32), so op(r0, r1) is the
+// pairwise reduction -- the same value, bit for bit, in both lanes.
+__device__ inline float quad_max(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float quad_sum(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Hide a pointer's provenance from the optimiser (an empty asm that "may
+// change" the register), so it is not re-derived from a shared base plus a
+// large per-access constant.
+template <typename P>
+__device__ inline void opaque(P *&p)
+{
+    asm volatile("" : "+v"(p));
+}
+
+// A raw buffer resource over one (b, h) map of a [B, heads, H, W, ...] tensor.
+__device__ inline __amdgpu_buffer_rsrc_t map_rsrc(const void *base, int64_t map_base,
+                                                  unsigned pixel_bytes, unsigned map_bytes)
+{
+    const char *p = static_cast<const char *>(base) + map_base * pixel_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, (int)map_bytes,
+                                             (int)kRsrcWord3);
+}
+
+}  // namespace
+}  // namespace na2d
