@@ -82,7 +82,7 @@ struct Args {
     float c;               // log2(e) / sqrt(d)
 };
 
-template <int QY, int QX, int NCB, int RPC, int NW = kWaves>
+template <int QY, int QX, int NCB, int RPC, int NW = kWaves, bool CT = true>
 struct Shape {
     static constexpr int NT = 64 * NW;              // threads per workgroup
     static constexpr int TY = QY * NW;              // tile rows
@@ -92,8 +92,9 @@ struct Shape {
     static constexpr int P = NC + QX - 1;           // interior bias table pitch
     static constexpr int PC = 2 * NC - 1;           // class table pitch
     // class tables (one per column class, see stage_bias) for one 16-column
-    // block and k <= 9; otherwise a general table plus an interior table
-    static constexpr bool CLS = NCB == 1 && QX == 8;
+    // block of 8-query-wide subtiles when CT allows them; otherwise a general
+    // table plus an interior table
+    static constexpr bool CLS = CT && NCB == 1 && QX == 8;
     static_assert(QY * QX == 16, "a wave owns 16 queries");
     static_assert(BPC % 2 == 0, "P.V consumes key blocks in pairs");
 };
@@ -312,12 +313,12 @@ __device__ inline void stage_tile(const Args &a, const Tile &t, unsigned char *s
 //  kGeneral:  split layout, general table with per-row / per-column indices.
 enum { kClass = 0, kInterior = 1, kGeneral = 2 };
 
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int MODE, int WM>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int MODE, int WM, bool CT>
 __device__ inline void attend(const Args &a, const Tile &t, const unsigned char *smem,
                               const float *btab, int lr, int wave, int ry, int lane,
                               const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum)
 {
-    using S = Shape<QY, QX, NCB, RPC>;
+    using S = Shape<QY, QX, NCB, RPC, kWaves, CT>;
     using FragT = typename Frag<T>::type;
     constexpr int P = S::P, PC = S::PC;
     const int ks = KS ? KS : a.ks;
@@ -488,18 +489,18 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 
 // One wave's share of a tile: choose its candidate key rows and the bias
 // path, leave o / lsum for store_out.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT = true>
 __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned char *smem,
                                    const float *btab, int lr, int wave, int lane,
                                    const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum)
 {
-    using S = Shape<QY, QX, NCB, RPC>;
+    using S = Shape<QY, QX, NCB, RPC, kWaves, CT>;
     const int ks = KS ? KS : a.ks, H = a.H, W = a.W, r = ks >> 1;
     const int nr = wave_rows(QY, RPC, ks);
     const int y1 = t.y0 + QY * wave;
     const int ry = max(t.hy0, min(window_start<WM>(min(y1, H - 1), ks, H), t.hy0 + t.hr - nr));
     if constexpr (S::CLS) {
-        attend<T, QY, QX, NCB, RPC, KS, kClass, WM>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
+        attend<T, QY, QX, NCB, RPC, KS, kClass, WM, CT>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
                                                     lsum);
     } else {
         // no query window clamped (SASA windows never are), and the candidate
@@ -509,10 +510,10 @@ __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned 
                                 t.x0 + QX - 1 + r <= W - 1);
         const bool interior = unclamped && ry == y1 - r && t.cx == t.x0 - r;
         if (interior)
-            attend<T, QY, QX, NCB, RPC, KS, kInterior, WM>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
+            attend<T, QY, QX, NCB, RPC, KS, kInterior, WM, CT>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
                                                        lsum);
         else
-            attend<T, QY, QX, NCB, RPC, KS, kGeneral, WM>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
+            attend<T, QY, QX, NCB, RPC, KS, kGeneral, WM, CT>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
                                                       lsum);
     }
 }
@@ -546,10 +547,10 @@ __device__ inline void store_out(const Args &a, const Tile &t, int wave, int lan
 // workgroups sharing an L2 work on neighbouring tiles).  Per tile: attend,
 // barrier, issue the next tile's copies, store this tile's outputs, wait for
 // the copies only, barrier.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT>
 __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
 {
-    using S = Shape<QY, QX, NCB, RPC>;
+    using S = Shape<QY, QX, NCB, RPC, kWaves, CT>;
     using FragT = typename Frag<T>::type;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
     while (true) {
         floatx4 o[2];
         float lsum;
-        attend_wave<T, QY, QX, NCB, RPC, KS, WM>(a, t, smem, bt, lr, wave, lane, qf, o, lsum);
+        attend_wave<T, QY, QX, NCB, RPC, KS, WM, CT>(a, t, smem, bt, lr, wave, lane, qf, o, lsum);
         const Tile done = t;
         const unsigned next = tile + step;
         __syncthreads();  // every wave is done reading the LDS copy
@@ -674,10 +675,10 @@ __device__ inline void write_tile_regs(unsigned char *smem, int wave, int lane,
     }
 }
 
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM, bool CT>
 __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
 {
-    using S = Shape<QY, QX, NCB, RPC, NW>;
+    using S = Shape<QY, QX, NCB, RPC, NW, CT>;
     using FragT = typename Frag<T>::type;
     constexpr int NR = wave_rows(QY, RPC, KS);
     constexpr int LR = S::TY + KS - 1 > NR ? S::TY + KS - 1 : NR;
@@ -725,7 +726,8 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
         float lsum = 1.f;
         if (t.y0 + QY * wave < a.H) {  // the bottom tile row may leave whole waves idle
             const FragT qf = __builtin_bit_cast(FragT, *qfrag);
-            attend_wave<T, QY, QX, NCB, RPC, KS, WM>(a, t, halo, btab, LR, wave, lane, qf, o, lsum);
+            attend_wave<T, QY, QX, NCB, RPC, KS, WM, CT>(a, t, halo, btab, LR, wave, lane, qf, o,
+                                                         lsum);
         }
         const Tile done = t;
         const bool more = next < end;
@@ -800,7 +802,8 @@ bool make_args(const Problem &p, Args &a)
 // workgroups: the memory system wants every slot's loads in flight), each
 // XCD given its own contiguous tile range when there are enough workgroups.
 template <typename K>
-hipError_t launch_persistent(K kern, Args &a, int threads, size_t lds, hipStream_t stream)
+hipError_t launch_persistent(K kern, Args &a, int threads, size_t lds, hipStream_t stream,
+                             bool flat = false)
 {
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -813,10 +816,10 @@ hipError_t launch_persistent(K kern, Args &a, int threads, size_t lds, hipStream
     const int cus = device_cus();
     if (per_cu <= 0 || cus <= 0) return hipErrorInvalidConfiguration;
     uint64_t grid = (uint64_t)cus * per_cu;
-    if (grid > a.ntiles) grid = a.ntiles;
+    if (flat || grid > a.ntiles) grid = a.ntiles;  // flat: one tile per workgroup
     a.xcd_split = 0;
     if (grid >= 64) {
-        grid &= ~7ull;
+        grid = flat ? (grid + 7) & ~7ull : grid & ~7ull;
         a.xcd_split = 1;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, stream, a);
@@ -824,26 +827,27 @@ hipError_t launch_persistent(K kern, Args &a, int threads, size_t lds, hipStream
 }
 
 // General kernel sizes: the LDS-DMA kernel with 4 waves per workgroup.
-template <typename T, int QY, int QX, int NCB, int RPC, int WM>
+template <typename T, int QY, int QX, int NCB, int RPC, int WM, bool CT = true, bool FLAT = false>
 hipError_t launch_dma(const Problem &p, hipStream_t stream)
 {
-    using S = Shape<QY, QX, NCB, RPC>;
+    using S = Shape<QY, QX, NCB, RPC, kWaves, CT>;
     Args a;
     if (!make_args<S, QY, RPC>(p, a)) return hipErrorInvalidConfiguration;
     const int nr = wave_rows(QY, RPC, p.ksize);
     const size_t lds =
         lds_bytes(a.lr, S::NC, bias_floats(S::CLS, p.ksize, nr, QY, QX, S::NC, RPC));
-    return launch_persistent(na2d_mfma_kernel<T, QY, QX, NCB, RPC, 0, WM>, a, S::NT, lds, stream);
+    return launch_persistent(na2d_mfma_kernel<T, QY, QX, NCB, RPC, 0, WM, CT>, a, S::NT, lds,
+                             stream, FLAT);
 }
 
 // A compile-time kernel size: the register-prefetch kernel with NW waves.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM, bool CT = true>
 hipError_t launch_pipe(const Problem &p, hipStream_t stream)
 {
-    using S = Shape<QY, QX, NCB, RPC, NW>;
+    using S = Shape<QY, QX, NCB, RPC, NW, CT>;
     Args a;
     if (!make_args<S, QY, RPC>(p, a)) return hipErrorInvalidConfiguration;
-    return launch_persistent(na2d_mfma_pipe_kernel<T, QY, QX, NCB, RPC, KS, NW, WM>, a, S::NT, 0,
+    return launch_persistent(na2d_mfma_pipe_kernel<T, QY, QX, NCB, RPC, KS, NW, WM, CT>, a, S::NT, 0,
                              stream);
 }
 
@@ -851,7 +855,7 @@ template <typename T, int WM>
 hipError_t launch_typed(const Problem &p, hipStream_t stream)
 {
     const int ks = p.ksize;
-    if (ks == 7) return launch_pipe<T, 2, 8, 1, 8, 7, 4, WM>(p, stream);
+    if (ks == 7) return launch_pipe<T, 2, 8, 1, 8, 7, 4, WM, false>(p, stream);
     if (ks <= 9) return launch_dma<T, 2, 8, 1, 2, WM>(p, stream);
     if (ks <= 13) return launch_dma<T, 4, 4, 1, 8, WM>(p, stream);
     return launch_dma<T, 2, 8, 2, 2, WM>(p, stream);
