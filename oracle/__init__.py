@@ -23,6 +23,8 @@ SOURCE = os.path.join(_HERE, "na2d_oracle.c")
 LIBRARY = os.path.join(_HERE, "libna2d_oracle.so")
 ND_SOURCE = os.path.join(_HERE, "na_nd_oracle.c")
 ND_LIBRARY = os.path.join(_HERE, "libna_nd_oracle.so")
+BWD_SOURCE = os.path.join(_HERE, "na2d_bwd_oracle.c")
+BWD_LIBRARY = os.path.join(_HERE, "libna2d_bwd_oracle.so")
 
 NA, SASA = 0, 1  # window modes of the N-axis oracle
 
@@ -42,6 +44,8 @@ def build(force: bool = True) -> str:
         compile_oracle(SOURCE, LIBRARY)
     if force or not os.path.exists(ND_LIBRARY):
         compile_oracle(ND_SOURCE, ND_LIBRARY)
+    if force or not os.path.exists(BWD_LIBRARY):
+        compile_oracle(BWD_SOURCE, BWD_LIBRARY)
     return LIBRARY
 
 
@@ -210,3 +214,50 @@ def sasa2d_forward(q, k, v, rpb, ksize: int, idx=None, nthreads: int = 0, orc=No
     out = orc.forward(np.reshape(q, sh), np.reshape(k, sh), np.reshape(v, sh), r, (1, ksize, ksize),
                       SASA, idx, nthreads)
     return out if idx is not None else out.reshape(q.shape)
+
+
+class OracleBwd:
+    """ctypes front of the NA2D gradient oracle (na2d_bwd_oracle.c)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        lib.na2d_oracle_backward_f64.argtypes = [P] * 9 + [I] * 7
+        lib.na2d_oracle_backward_f64.restype = I
+        self.lib = lib
+        self.path = path
+
+    def backward(self, q, k, v, rpb, dout, ksize: int, nthreads: int = 0):
+        """Gradients (dq, dk, dv, drpb) of sum(dout * NA2D(q, k, v, rpb)); drpb is
+        None when rpb is None."""
+        q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+        assert q.ndim == 5 and q.shape == k.shape == v.shape == g.shape
+        B, heads, H, W, d = q.shape
+        drpb = None
+        if rpb is not None:
+            rpb = _f64(rpb)
+            assert rpb.shape == (heads, 2 * ksize - 1, 2 * ksize - 1)
+            drpb = np.empty_like(rpb)
+        dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+        rc = self.lib.na2d_oracle_backward_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(g),
+                                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drpb), B, heads,
+                                               H, W, d, ksize, nthreads)
+        if rc != 0:
+            raise ValueError("backward oracle rejected sizes %s k=%d" % (q.shape, ksize))
+        return dq, dk, dv, drpb
+
+
+_default_bwd = None
+
+
+def default_bwd() -> OracleBwd:
+    global _default_bwd
+    if _default_bwd is None:
+        if not os.path.exists(BWD_LIBRARY):
+            build()
+        _default_bwd = OracleBwd(BWD_LIBRARY)
+    return _default_bwd
+
+
+def na2d_backward(q, k, v, rpb, dout, ksize: int, nthreads: int = 0):
+    return default_bwd().backward(q, k, v, rpb, dout, ksize, nthreads)
