@@ -116,6 +116,97 @@ def cpu_baseline(w, x, seconds: float = 10.0):
                       % (n, w.name, done // n, el)}
 
 
+def backward_bytes(w) -> int:
+    """Bytes the gradients must move: read q, k, v, out and dout, write dq, dk,
+    dv once, read the bias table and write its gradient."""
+    es = 4 if w.dtype == "f32" else 2
+    return w.queries * (3 * w.d * es + 2 * 4 * w.d + 3 * 4 * w.d) + 2 * 4 * math.prod(w.rpb_shape)
+
+
+def bench_backward(args, w, wname, lib, dev, dtype_code):
+    import torch
+    from vision_sliding_window_amd import na2d
+    from vision_sliding_window_amd.inputs import workload_inputs
+    x = workload_inputs(w, seed=0)
+    set_bytes = backward_bytes(w)
+    nsets = max(1, math.ceil(args.min_footprint_gib * 2 ** 30 / set_bytes))
+    rpb = x.rpb.to(dev)
+    q0, k0, v0 = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    out0 = na2d.forward(q0, k0, v0, rpb, w.k)
+    g0 = torch.randn(w.shape, generator=torch.Generator().manual_seed(1)).to(dev)
+    ws_bytes = na2d.na2d_backward_workspace_bytes(w.B, w.heads, w.H, w.W)
+    f32 = dict(dtype=torch.float32, device=dev)
+    sets = []
+    for i in range(nsets):
+        c = (lambda t: t.clone()) if i else (lambda t: t)
+        sets.append((c(q0), c(k0), c(v0), c(out0), c(g0), torch.empty(w.shape, **f32),
+                     torch.empty(w.shape, **f32), torch.empty(w.shape, **f32),
+                     torch.empty(rpb.shape, **f32), torch.empty(ws_bytes // 4, **f32)))
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def launch(i):
+        q, k, v, out, g, dq, dk, dv, drpb, ws = sets[i % nsets]
+        st = lib.na2d_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
+                               out.data_ptr(), g.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), drpb.data_ptr(), ws.data_ptr(), w.B, w.heads, w.H,
+                               w.W, w.d, w.k, dtype_code, sptr)
+        if st != 0:
+            raise RuntimeError("na2d_backward failed: %s" % na2d.na2d_strerror(st))
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    gbs = set_bytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "NA2D bwd queries/s and achieved HBM GB/s (%% roofline), %s" % wname,
+        "value": round(w.queries / (ms * 1e-3), 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic: Q,K,V ~ N(0,1), RPB ~ N(0,0.02), dout ~ N(0,1)",
+        "config": {"workload": wname, "pass": "backward", "B": w.B, "heads": w.heads, "H": w.H,
+                   "W": w.W, "d": w.d, "k": w.k, "kernel": "valu", "rotating_sets": nsets,
+                   "algorithmic_bytes_per_step": set_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_backward(w, x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_backward(w, x, seconds):
+    """The fp64 gradient oracle as it stands on the host cores: whole-workload
+    passes until about `seconds` have passed (at least one)."""
+    import numpy as np
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        cores = min(cores, int(env))
+    g = np.random.default_rng(1).standard_normal(x.q64.shape)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.na2d_backward(x.q64, x.k64, x.v64, x.rpb64, g, w.k, nthreads=cores)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n * w.queries / el, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": "%d whole pass(es) over %s, fp64, %.1f s" % (n, w.name, el)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +219,8 @@ def main():
     ap.add_argument("--hot", action="store_true",
                     help="also time one cache-resident input set (reported separately)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the NA2D gradients (na2d_backward) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device-to-device copy of MIB "
                          "MiB a few times (calibrates HBM byte counters under rocprofv3)")
@@ -171,6 +264,12 @@ def main():
     grid = (w.depth, w.H, w.W)
     window = {"na1d": (1, 1, w.k), "na3d": (w.k, w.k, w.k)}.get(w.op, (1, w.k, w.k))
     mode = na2d.NA_WINDOW_SASA if w.op == "sasa2d" else na2d.NA_WINDOW_NA
+
+    if args.backward:
+        if w.op != "na2d":
+            print("--backward covers the NA2D workloads", file=sys.stderr)
+            sys.exit(2)
+        return bench_backward(args, w, wname, lib, dev, dtype_code)
 
     x = workload_inputs(w, seed=0)
     set_bytes = algorithmic_bytes(w)

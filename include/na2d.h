@@ -165,6 +165,40 @@ int na3d_forward(const void *q, const void *k, const void *v, const float *rpb, 
 int sasa2d_forward(const void *q, const void *k, const void *v, const float *rpb, float *out,
                    int B, int heads, int H, int W, int d, int ksize, int dtype, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Gradients of the NA2D forward (the training half; NATTEN computes them
+ * for QK+B and AV, qiita article, section "NATTEN").
+ *
+ * For L with dL/dout = dout, writes dq, dk, dv = dL/dq, dL/dk, dL/dv
+ * ([B, heads, H, W, d] float32, overwritten) and, when rpb is not NULL,
+ * drpb = dL/drpb ([heads, 2k-1, 2k-1] float32, overwritten; it must be NULL
+ * when rpb is).  q, k, v, rpb, ksize and dtype are those of the forward call;
+ * out is its float32 output and dout is float32 [B, heads, H, W, d].
+ *
+ * `workspace` is caller-owned device memory of na2d_backward_workspace_bytes
+ * bytes (8 per query, 16-byte aligned): the first kernel leaves each query's
+ * softmax statistics there for the second, so no k*k attention tensor is
+ * stored.  d must be 16, 32, 64 or 128 and ksize <= NA2D_VALU_MAX_KSIZE.
+ * The gradient of the bias table is accumulated with float atomics, so its
+ * last bits may differ from call to call; everything else is deterministic.
+ * No output may overlap an input or another output.  Other conventions as
+ * for na2d_forward.
+ * ------------------------------------------------------------------------ */
+int na2d_backward(const void *q, const void *k, const void *v, const float *rpb,
+                  const float *out, const float *dout, float *dq, float *dk, float *dv,
+                  float *drpb, void *workspace, int B, int heads, int H, int W, int d,
+                  int ksize, int dtype, void *stream);
+
+/* Bytes of workspace na2d_backward needs (0 if the sizes are invalid). */
+long long na2d_backward_workspace_bytes(int B, int heads, int H, int W);
+
+/* Host-only check of na2d_backward's arguments (no HIP call). */
+int na2d_backward_check_args(const void *q, const void *k, const void *v, const float *rpb,
+                             const float *out, const float *dout, const float *dq,
+                             const float *dk, const float *dv, const float *drpb,
+                             const void *workspace, int B, int heads, int H, int W, int d,
+                             int ksize, int dtype);
+
 /* Static text for a status code. */
 const char *na2d_strerror(int status);
 

@@ -191,3 +191,34 @@ def test_nd_wrappers_reject_before_launch():
     assert na2d.na3d_forward(Q, K, V, RPB, OUT, 2, 2, 4, 9, 9, 32, 5, f16, None) == na2d.NA2D_ERR_KSIZE
     assert na2d.sasa2d_forward(Q, K, V, RPB, OUT, 2, 2, 9, 9, 32, 6, f16, None) == na2d.NA2D_ERR_KSIZE
     assert na2d.sasa2d_forward(Q, K, V, RPB, Q, 2, 2, 9, 9, 32, 5, f16, None) == na2d.NA2D_ERR_ALIAS
+
+
+DQ, DK, DV, DRPB, WS, DOUT = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000, 0xB0000000
+
+
+def check_bwd(B=2, heads=2, H=14, W=15, d=32, ksize=7, dtype=na2d.NA2D_F16, **ptr):
+    p = dict(q=Q, k=K, v=V, rpb=RPB, out=OUT, dout=DOUT, dq=DQ, dk=DK, dv=DV, drpb=DRPB, ws=WS)
+    p.update(ptr)
+    return na2d.na2d_backward_check_args(p["q"], p["k"], p["v"], p["rpb"], p["out"], p["dout"],
+                                         p["dq"], p["dk"], p["dv"], p["drpb"], p["ws"], B, heads,
+                                         H, W, d, ksize, dtype)
+
+
+def test_backward_args():
+    assert check_bwd() == na2d.NA2D_OK
+    assert check_bwd(rpb=None, drpb=None) == na2d.NA2D_OK
+    assert check_bwd(drpb=None) == na2d.NA2D_ERR_NULL        # bias without its gradient
+    assert check_bwd(rpb=None) == na2d.NA2D_ERR_NULL         # gradient without a bias
+    assert check_bwd(ws=None) == na2d.NA2D_ERR_NULL
+    assert check_bwd(dout=None) == na2d.NA2D_ERR_NULL
+    assert check_bwd(ksize=8) == na2d.NA2D_ERR_KSIZE
+    assert check_bwd(d=48) == na2d.NA2D_ERR_UNSUPPORTED
+    assert check_bwd(dq=DQ + 4) == na2d.NA2D_ERR_ALIGN
+    assert check_bwd(dq=Q) == na2d.NA2D_ERR_ALIAS             # output on an input
+    assert check_bwd(dk=DQ + 64) == na2d.NA2D_ERR_ALIAS       # two outputs overlap
+    assert check_bwd(ws=DOUT + 16) == na2d.NA2D_ERR_ALIAS
+    assert na2d.na2d_backward_workspace_bytes(2, 2, 14, 15) == 2 * 2 * 14 * 15 * 8
+    assert na2d.na2d_backward_workspace_bytes(0, 2, 14, 15) == 0
+    st = na2d.na2d_backward(Q, K, V, RPB, OUT, DOUT, DQ, DK, DV, DRPB, WS, 2, 2, 14, 15, 32, 17,
+                            na2d.NA2D_F16, None)
+    assert st == na2d.NA2D_ERR_KSIZE                          # rejected before any launch

@@ -213,6 +213,74 @@ extern "C" int sasa2d_forward(const void *q, const void *k, const void *v, const
                       NA2D_ALGO_AUTO, stream);
 }
 
+namespace {
+
+int check_backward(const void *q, const void *k, const void *v, const float *rpb,
+                   const float *out, const float *dout, const float *dq, const float *dk,
+                   const float *dv, const float *drpb, const void *ws, int B, int heads, int H,
+                   int W, int d, int ksize, int dtype)
+{
+    if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
+    if (!q || !k || !v || !out || !dout || !dq || !dk || !dv || !ws) return NA2D_ERR_NULL;
+    if (!rpb != !drpb) return NA2D_ERR_NULL;  // a bias gradient exactly when there is a bias
+    const Nd n = nd_2d(B, heads, H, W, d, ksize, NA_WINDOW_NA);
+    const int st = check_sizes(n);
+    if (st != NA2D_OK) return st;
+    const void *ptrs[11] = {q, k, v, rpb, out, dout, dq, dk, dv, drpb, ws};
+    for (const void *p : ptrs)
+        if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return NA2D_ERR_ALIGN;
+    const uint64_t queries = (uint64_t)B * heads * H * W, elems = queries * d;
+    const uint64_t in_b = elems * elem_size(dtype), f_b = elems * 4, ws_b = queries * 8;
+    const uint64_t rpb_b = (uint64_t)heads * (2 * ksize - 1) * (2 * ksize - 1) * 4;
+    struct Span { const void *p; uint64_t n; };
+    const Span outs[5] = {{dq, f_b}, {dk, f_b}, {dv, f_b}, {drpb, rpb_b}, {ws, ws_b}};
+    const Span ins[6] = {{q, in_b}, {k, in_b}, {v, in_b}, {rpb, rpb_b}, {out, f_b}, {dout, f_b}};
+    for (int i = 0; i < 5; ++i) {
+        for (const Span &in : ins)
+            if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return NA2D_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return NA2D_ERR_ALIAS;
+    }
+    if (!valu_supports(n)) return NA2D_ERR_UNSUPPORTED;
+    return NA2D_OK;
+}
+
+}  // namespace
+
+extern "C" int na2d_backward_check_args(const void *q, const void *k, const void *v,
+                                        const float *rpb, const float *out, const float *dout,
+                                        const float *dq, const float *dk, const float *dv,
+                                        const float *drpb, const void *workspace, int B,
+                                        int heads, int H, int W, int d, int ksize, int dtype)
+{
+    return check_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads, H, W,
+                          d, ksize, dtype);
+}
+
+extern "C" long long na2d_backward_workspace_bytes(int B, int heads, int H, int W)
+{
+    if (B <= 0 || heads <= 0 || H <= 0 || W <= 0) return 0;
+    return (long long)B * heads * H * W * 8;
+}
+
+extern "C" int na2d_backward(const void *q, const void *k, const void *v, const float *rpb,
+                             const float *out, const float *dout, float *dq, float *dk,
+                             float *dv, float *drpb, void *workspace, int B, int heads, int H,
+                             int W, int d, int ksize, int dtype, void *stream)
+{
+    const int st = check_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads,
+                                  H, W, d, ksize, dtype);
+    if (st != NA2D_OK) return st;
+    const na2d::BwdProblem p{q,  k,  v,    rpb,       out, dout,  dq, dk, dv,
+                             drpb, workspace, B, heads, H, W, d, ksize, dtype};
+    const hipError_t e = na2d::launch_backward(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        g_last_error = hipGetErrorString(e);
+        return NA2D_ERR_HIP;
+    }
+    return NA2D_OK;
+}
+
 extern "C" const char *na2d_strerror(int status)
 {
     switch (status) {

@@ -17,10 +17,20 @@ struct Problem {
     int depth, kd, kh, kw, mode;
 };
 
+// One validated backward problem (include/na2d.h, na2d_backward).
+struct BwdProblem {
+    const void *q, *k, *v;
+    const float *rpb, *out, *dout;
+    float *dq, *dk, *dv, *drpb;
+    void *workspace;
+    int B, heads, H, W, d, ksize, dtype;
+};
+
 // Launchers; each returns the HIP status of its launch.  The arguments have
 // been checked by the caller.
 hipError_t launch_valu(const Problem &p, hipStream_t stream);
 hipError_t launch_mfma(const Problem &p, hipStream_t stream);     // square 2D windows
 hipError_t launch_mfma_1d(const Problem &p, hipStream_t stream);  // NA1D
+hipError_t launch_backward(const BwdProblem &p, hipStream_t stream);
 
 }  // namespace na2d

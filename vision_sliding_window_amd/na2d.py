@@ -32,7 +32,8 @@ NA2D_ERR_ALGO = -9
 
 EXPORTS = ["na2d_forward", "na2d_forward_ex", "na2d_check_args", "na2d_select_algo",
            "na2d_strerror", "na2d_last_error", "na2d_version", "na_forward_nd",
-           "na_check_args_nd", "na1d_forward", "na3d_forward", "sasa2d_forward"]
+           "na_check_args_nd", "na1d_forward", "na3d_forward", "sasa2d_forward",
+           "na2d_backward", "na2d_backward_workspace_bytes", "na2d_backward_check_args"]
 
 TORCH_DTYPE_CODE = {torch.float32: NA2D_F32, torch.float16: NA2D_F16, torch.bfloat16: NA2D_BF16}
 
@@ -81,6 +82,12 @@ def load() -> ctypes.CDLL:
         lib.na3d_forward.restype = I
         lib.sasa2d_forward.argtypes = [P, P, P, P, P] + [I] * 7 + [P]
         lib.sasa2d_forward.restype = I
+        lib.na2d_backward.argtypes = [P] * 11 + [I] * 7 + [P]
+        lib.na2d_backward.restype = I
+        lib.na2d_backward_workspace_bytes.argtypes = [I] * 4
+        lib.na2d_backward_workspace_bytes.restype = ctypes.c_longlong
+        lib.na2d_backward_check_args.argtypes = [P] * 11 + [I] * 7
+        lib.na2d_backward_check_args.restype = I
         _lib = lib
     return _lib
 
@@ -146,6 +153,24 @@ def na3d_forward(q, k, v, rpb, out, B, heads, D, H, W, d, ksize, dtype, stream=N
 def sasa2d_forward(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, stream=None) -> int:
     return load().sasa2d_forward(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out), B, heads,
                                  H, W, d, ksize, dtype, _stream(stream))
+
+
+def na2d_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads, H, W, d, ksize,
+                  dtype, stream=None) -> int:
+    return load().na2d_backward(*(_addr(t) for t in (q, k, v, rpb, out, dout, dq, dk, dv, drpb,
+                                                     workspace)),
+                                B, heads, H, W, d, ksize, dtype, _stream(stream))
+
+
+def na2d_backward_workspace_bytes(B, heads, H, W) -> int:
+    return load().na2d_backward_workspace_bytes(B, heads, H, W)
+
+
+def na2d_backward_check_args(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads, H, W,
+                             d, ksize, dtype) -> int:
+    return load().na2d_backward_check_args(*(_addr(t) for t in (q, k, v, rpb, out, dout, dq, dk,
+                                                                dv, drpb, workspace)),
+                                           B, heads, H, W, d, ksize, dtype)
 
 
 def na2d_strerror(status: int) -> str:
@@ -255,3 +280,28 @@ def forward_nd(q, k, v, rpb, window, mode=NA_WINDOW_NA, algo=NA2D_ALGO_AUTO, out
     if st != NA2D_OK:
         raise NA2DError(st, na2d_last_error() if st == NA2D_ERR_HIP else "")
     return out
+
+
+def backward(q, k, v, rpb, out, dout, ksize: int, stream=None):
+    """Gradients (dq, dk, dv, drpb) of the NA2D forward on device tensors: q, k,
+    v, rpb as for ``forward``, out its float32 output, dout float32 of out's
+    shape.  drpb is None when rpb is None.  Allocates the outputs and the
+    workspace with torch."""
+    for t in (q, k, v):
+        if not (t.is_cuda and t.is_contiguous() and t.dim() == 5):
+            raise ValueError("q, k, v must be contiguous 5-d GPU tensors [B, heads, H, W, d]")
+    for t in (out, dout):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 and t.shape == q.shape):
+            raise ValueError("out and dout must be contiguous float32 GPU tensors shaped like q")
+    B, heads, H, W, d = q.shape
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty(q.shape, **f32), torch.empty(q.shape, **f32), torch.empty(q.shape, **f32)
+    drpb = None if rpb is None else torch.empty(rpb.shape, **f32)
+    ws = torch.empty(max(1, na2d_backward_workspace_bytes(B, heads, H, W) // 4), **f32)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = na2d_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, ws, B, heads, H, W, d, ksize,
+                       TORCH_DTYPE_CODE[q.dtype], stream)
+    if st != NA2D_OK:
+        raise NA2DError(st, na2d_last_error() if st == NA2D_ERR_HIP else "")
+    return dq, dk, dv, drpb
