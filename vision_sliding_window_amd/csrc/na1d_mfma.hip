@@ -30,6 +30,7 @@
 #include "na2d.h"
 #include "na2d_launch.h"
 #include "na_mfma_util.h"
+#include "na_xcd.h"
 
 #include <hip/hip_runtime.h>
 
@@ -49,6 +50,7 @@ struct Args1 {
     float *out;
     int heads, L, ks;
     int tiles_per_seq;
+    unsigned ntiles;
     float c;  // log2(e) / sqrt(d)
 };
 
@@ -77,8 +79,10 @@ __global__ __launch_bounds__(kT1) void na1d_mfma_kernel(Args1 a)
     __shared__ float braw[kMaxRaw];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int seq = blockIdx.x / a.tiles_per_seq;              // b * heads + h
-    const int x0 = (blockIdx.x - seq * a.tiles_per_seq) * kTQ;  // first query of the tile
+    const unsigned tile = xcd_tile(blockIdx.x, gridDim.x);  // neighbouring tiles share an L2
+    if (tile >= a.ntiles) return;
+    const int seq = tile / a.tiles_per_seq;                 // b * heads + h
+    const int x0 = (tile - seq * a.tiles_per_seq) * kTQ;    // first query of the tile
     const int h = seq % a.heads;
     const int ks = a.ks, L = a.L;
     const int64_t base = (int64_t)seq * L;
@@ -223,8 +227,10 @@ hipError_t launch_ncb(const Problem &p, hipStream_t stream)
     a.tiles_per_seq = (p.W + kTQ - 1) / kTQ;
     a.c = 1.4426950408889634f / sqrtf(32.f);
     const uint64_t blocks = (uint64_t)p.B * p.heads * a.tiles_per_seq;
-    if (blocks == 0 || blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((na1d_mfma_kernel<T, NCB>), dim3((unsigned)blocks), dim3(kT1), 0, stream, a);
+    if (blocks == 0 || xcd_grid(blocks) > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    a.ntiles = (unsigned)blocks;
+    hipLaunchKernelGGL((na1d_mfma_kernel<T, NCB>), dim3((unsigned)xcd_grid(blocks)), dim3(kT1), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

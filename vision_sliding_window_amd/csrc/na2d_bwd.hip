@@ -18,6 +18,7 @@
 // [j - k + 1, j]; it is found by scanning the 2k - 1 positions around j.
 #include "na2d.h"
 #include "na2d_launch.h"
+#include "na_xcd.h"
 
 #include <hip/hip_runtime.h>
 
@@ -61,6 +62,7 @@ struct BwdArgs {
     float2 *ws;  // per query: (log2-sum-exp of the log2-scaled logits, g . o)
     int heads, H, W, ks;
     int blocks_per_map;
+    unsigned nblocks;
     float c;      // log2(e) / sqrt(d): logits in log2 units
     float scale;  // 1 / sqrt(d)
 };
@@ -77,7 +79,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreadsB) void bwd_query_kernel(BwdArgs a)
 {
     __shared__ float dbias[kLdsBias];
-    const int map = blockIdx.x / a.blocks_per_map;  // b * heads + h
+    const unsigned blk = xcd_tile(blockIdx.x, gridDim.x);  // neighbouring blocks share an L2
+    if (blk >= a.nblocks) return;  // uniform per workgroup, before any barrier
+    const int map = blk / a.blocks_per_map;  // b * heads + h
     const int h = map % a.heads;
     const int H = a.H, W = a.W, ks = a.ks, nb = 2 * ks - 1;
     const bool lds_bias = a.drpb && nb * nb <= kLdsBias;
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(kThreadsB) void bwd_query_kernel(BwdArgs a)
         for (int e = threadIdx.x; e < nb * nb; e += kThreadsB) dbias[e] = 0.f;
     __syncthreads();
 
-    const int pix = (blockIdx.x - map * a.blocks_per_map) * kThreadsB + threadIdx.x;
+    const int pix = (blk - map * a.blocks_per_map) * kThreadsB + threadIdx.x;
     if (pix < H * W) {
         const int y = pix / W, x = pix - y * W;
         const int64_t base = (int64_t)map * H * W;
@@ -171,10 +175,12 @@ __global__ __launch_bounds__(kThreadsB) void bwd_query_kernel(BwdArgs a)
 template <typename T, int D>
 __global__ __launch_bounds__(kThreadsB) void bwd_key_kernel(BwdArgs a)
 {
-    const int map = blockIdx.x / a.blocks_per_map;
+    const unsigned blk = xcd_tile(blockIdx.x, gridDim.x);
+    if (blk >= a.nblocks) return;
+    const int map = blk / a.blocks_per_map;
     const int h = map % a.heads;
     const int H = a.H, W = a.W, ks = a.ks, nb = 2 * ks - 1;
-    const int pix = (blockIdx.x - map * a.blocks_per_map) * kThreadsB + threadIdx.x;
+    const int pix = (blk - map * a.blocks_per_map) * kThreadsB + threadIdx.x;
     if (pix >= H * W) return;
     const int ky = pix / W, kx = pix - ky * W;
     const int64_t base = (int64_t)map * H * W;
@@ -249,13 +255,15 @@ hipError_t launch_bwd_typed(const BwdProblem &p, hipStream_t stream)
     a.c = 1.4426950408889634f / sqrtf((float)D);
     a.scale = 1.f / sqrtf((float)D);
     const uint64_t blocks = (uint64_t)p.B * p.heads * a.blocks_per_map;
-    if (blocks == 0 || blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    if (blocks == 0 || xcd_grid(blocks) > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    a.nblocks = (unsigned)blocks;
     if (p.drpb) {  // the bias gradient accumulates: clear it first (a kernel, not a memset)
         const int n = p.heads * (2 * p.ksize - 1) * (2 * p.ksize - 1);
         hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p.drpb, n);
     }
-    hipLaunchKernelGGL((bwd_query_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreadsB), 0, stream, a);
-    hipLaunchKernelGGL((bwd_key_kernel<T, D>), dim3((unsigned)blocks), dim3(kThreadsB), 0, stream, a);
+    const dim3 grid((unsigned)xcd_grid(blocks));
+    hipLaunchKernelGGL((bwd_query_kernel<T, D>), grid, dim3(kThreadsB), 0, stream, a);
+    hipLaunchKernelGGL((bwd_key_kernel<T, D>), grid, dim3(kThreadsB), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@
 // exponentiating, which changes no value exactly.
 #include "na2d.h"
 #include "na2d_launch.h"
+#include "na_xcd.h"
 
 #include <hip/hip_runtime.h>
 
@@ -73,7 +74,9 @@ __global__ __launch_bounds__(256) void na_valu_kernel(
     const T *__restrict__ q, const T *__restrict__ kk, const T *__restrict__ v,
     const float *__restrict__ rpb, float *__restrict__ out, Grid g, float c, int64_t nq)
 {
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    // consecutive queries (neighbouring windows) stay on one XCD
+    const int64_t gid =
+        static_cast<int64_t>(xcd_tile(blockIdx.x, gridDim.x)) * blockDim.x + threadIdx.x;
     if (gid >= nq) return;
     int64_t t = gid;
     const int x = static_cast<int>(t % g.L2);
@@ -153,7 +156,7 @@ hipError_t launch_typed(const Problem &p, hipStream_t stream)
 {
     const int64_t nq = static_cast<int64_t>(p.B) * p.heads * p.depth * p.H * p.W;
     const int threads = 256;
-    const int64_t blocks = (nq + threads - 1) / threads;
+    const int64_t blocks = static_cast<int64_t>(xcd_grid((nq + threads - 1) / threads));
     const float c = 1.4426950408889634f / sqrtf(static_cast<float>(D));
     const Grid g{p.heads, p.depth, p.H, p.W, p.kd, p.kh, p.kw};
     hipLaunchKernelGGL((na_valu_kernel<T, D, MODE>), dim3(static_cast<unsigned>(blocks)),
