@@ -30,8 +30,16 @@ if ROOT not in sys.path:
 METRIC = "NA2D fwd queries/s and achieved HBM GB/s (% roofline), NAT-Tiny stage1 k=7"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
-KERNEL_SOURCES = {1: "na_valu.hip", 2: "na2d_mfma.hip"}
-KERNEL_SOURCES_1D = {1: "na_valu.hip", 2: "na1d_mfma.hip"}
+# kernel family -> its source (a committed traffic summary is used only when it
+# was taken on the source as it is now)
+KERNEL_SOURCES = {"na_valu": "na_valu.hip", "na2d_mfma": "na2d_mfma.hip",
+                  "na1d_mfma": "na1d_mfma.hip", "na2d_bwd": "na2d_bwd.hip"}
+
+
+def kernel_id(op: str, algo: int) -> str:
+    if algo == 1:
+        return "na_valu"
+    return "na1d_mfma" if op == "na1d" else "na2d_mfma"
 
 
 def algorithmic_bytes(w) -> int:
@@ -53,10 +61,12 @@ def source_digest(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(workload: str, algo_name: str, kernel_src: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the kernel source as it is now (else None)."""
-    path = os.path.join(ROOT, "profiles", "na2d_%s_%s_traffic.txt" % (algo_name, workload))
+def read_traffic(workload: str, kid: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    kernel family `kid` on `workload`, if it was taken on the kernel source as
+    it is now (else None)."""
+    kernel_src = KERNEL_SOURCES[kid]
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.txt" % (kid, workload))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -175,7 +185,9 @@ def bench_backward(args, w, wname, lib, dev, dtype_code):
                    "W": w.W, "d": w.d, "k": w.k, "kernel": "valu", "rotating_sets": nsets,
                    "algorithmic_bytes_per_step": set_bytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": (lambda t: None if t is None else int(t))(
+                         read_traffic(wname, "na2d_bwd"))},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_backward(w, x, args.cpu_seconds)
@@ -322,8 +334,7 @@ def main():
     value = w.queries / (ms * 1e-3)
     gbs = set_bytes / (ms * 1e-3) / 1e9
     tflops = algorithmic_flops(w) / (ms * 1e-3) / 1e12
-    traffic = read_traffic(wname, algo_name,
-                           (KERNEL_SOURCES_1D if w.op == "na1d" else KERNEL_SOURCES)[algo])
+    traffic = read_traffic(wname, kernel_id(w.op, algo))
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else int(traffic)}
