@@ -222,3 +222,19 @@ def test_backward_args():
     st = na2d.na2d_backward(Q, K, V, RPB, OUT, DOUT, DQ, DK, DV, DRPB, WS, 2, 2, 14, 15, 32, 17,
                             na2d.NA2D_F16, None)
     assert st == na2d.NA2D_ERR_KSIZE                          # rejected before any launch
+
+
+def test_holder_ranges_closed_form():
+    """The backward's key pass visits, per axis, the positions whose clamped
+    window holds key j: lo = 0 if j < k else j - k//2, hi = L - 1 if
+    j >= L - k else j + k//2 (the closed form in na2d_bwd.hip), which must be
+    exactly the brute-force set."""
+    def start(i, k, L):
+        return min(max(i - k // 2, 0), L - k)
+    for k in (1, 3, 5, 7, 9, 13, 25, 63):
+        for L in range(k, 3 * k + 5):
+            for j in range(L):
+                members = [i for i in range(L) if start(i, k, L) <= j < start(i, k, L) + k]
+                lo = 0 if j < k else j - k // 2
+                hi = L - 1 if j >= L - k else j + k // 2
+                assert members == list(range(lo, hi + 1)), (k, L, j)

@@ -15,7 +15,7 @@
 // query), from which the key kernel recomputes p_ij and dS_ij for every query
 // whose window holds its key.  Those queries form, on each axis, the
 // contiguous range of positions whose clamped window start lies in
-// [j - k + 1, j]; it is found by scanning the 2k - 1 positions around j.
+// [j - k + 1, j] (holders() gives its ends in closed form).
 #include "na2d.h"
 #include "na2d_launch.h"
 #include "na_xcd.h"
@@ -39,6 +39,20 @@ __device__ inline int window_start(int i, int ks, int L)
     int s = i - (ks >> 1);
     s = s < 0 ? 0 : s;
     return s > L - ks ? L - ks : s;
+}
+
+// The positions of an axis of length L whose clamped window of ks holds
+// position j: [lo, hi].  The window start s(i) = clamp(i - r, 0, L - ks) is
+// non-decreasing, so they are the i with j - ks + 1 <= s(i) <= j.  Low end:
+// if j < ks every window starting at 0 holds j, so lo = 0; otherwise s(i) >= 1
+// forces the unclamped branch s(i) = i - r, i >= j - r.  High end: if
+// j >= L - ks every window start (at most L - ks) is <= j, so hi = L - 1;
+// otherwise s(i) = i - r <= j, i <= j + r.
+__device__ inline void holders(int j, int ks, int L, int &lo, int &hi)
+{
+    const int r = ks >> 1;
+    lo = j < ks ? 0 : j - r;
+    hi = j >= L - ks ? L - 1 : j + r;
 }
 
 template <typename T, int D>
@@ -193,14 +207,11 @@ __global__ __launch_bounds__(kThreadsB) void bwd_key_kernel(BwdArgs a)
     float dkf[D], dvf[D];
 #pragma unroll
     for (int e = 0; e < D; ++e) dkf[e] = dvf[e] = 0.f;
-    const int y0 = max(0, ky - ks + 1), y1 = min(H - 1, ky + ks - 1);
-    const int x0 = max(0, kx - ks + 1), x1 = min(W - 1, kx + ks - 1);
+    int y0, y1, x0, x1;
+    holders(ky, ks, H, y0, y1);
+    holders(kx, ks, W, x0, x1);
     for (int y = y0; y <= y1; ++y) {
-        const int sy = window_start(y, ks, H);
-        if (ky < sy || ky >= sy + ks) continue;  // j is not in the windows of row y
         for (int x = x0; x <= x1; ++x) {
-            const int sx = window_start(x, ks, W);
-            if (kx < sx || kx >= sx + ks) continue;
             const int64_t qi = base + (int64_t)y * W + x;
             float qf[D], gf[D];
             load_row<T, D>(qq + qi * D, qf);
