@@ -90,6 +90,9 @@ enum {
 #define NA2D_MFMA_MAX_KSIZE 25
 /* Largest window of the NA1D matrix-core kernel (d = 32, 16-bit inputs). */
 #define NA1D_MFMA_MAX_KSIZE 63
+/* Largest window whose backward runs on the matrix cores (d = 32, 16-bit
+ * inputs); larger windows, fp32 and other head dims use the VALU kernels. */
+#define NA2D_BWD_MFMA_MAX_KSIZE 25
 
 /* Fused NA2D forward (CSDN page, section 3.1, Eq. 2-4), kernel chosen
  * automatically.  Sizes are element counts; see the conventions above. */

@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace na2d {
 namespace {
@@ -274,6 +275,12 @@ hipError_t launch_bwd_typed(const BwdProblem &p, hipStream_t stream)
     }
     const dim3 grid((unsigned)xcd_grid(blocks));
     hipLaunchKernelGGL((bwd_query_kernel<T, D>), grid, dim3(kThreadsB), 0, stream, a);
+    // the key pass runs on the matrix cores where they apply
+    if (!std::is_same<T, float>::value && D == 32 && p.ksize <= NA2D_BWD_MFMA_MAX_KSIZE) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_backward_kv_mfma(p, stream);
+    }
     hipLaunchKernelGGL((bwd_key_kernel<T, D>), grid, dim3(kThreadsB), 0, stream, a);
     return hipGetLastError();
 }

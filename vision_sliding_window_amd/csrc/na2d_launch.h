@@ -32,5 +32,6 @@ hipError_t launch_valu(const Problem &p, hipStream_t stream);
 hipError_t launch_mfma(const Problem &p, hipStream_t stream);     // square 2D windows
 hipError_t launch_mfma_1d(const Problem &p, hipStream_t stream);  // NA1D
 hipError_t launch_backward(const BwdProblem &p, hipStream_t stream);
+hipError_t launch_backward_kv_mfma(const BwdProblem &p, hipStream_t stream);  // key pass on MFMA
 
 }  // namespace na2d
