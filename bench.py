@@ -144,7 +144,7 @@ def bench_backward(args, w, wname, lib, dev, dtype_code):
     q0, k0, v0 = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     out0 = na2d.forward(q0, k0, v0, rpb, w.k)
     g0 = torch.randn(w.shape, generator=torch.Generator().manual_seed(1)).to(dev)
-    ws_bytes = na2d.na2d_backward_workspace_bytes(w.B, w.heads, w.H, w.W)
+    ws_bytes = na2d.na2d_backward_workspace_bytes(w.B, w.heads, w.H, w.W, w.k)
     f32 = dict(dtype=torch.float32, device=dev)
     sets = []
     for i in range(nsets):

@@ -179,11 +179,13 @@ int sasa2d_forward(const void *q, const void *k, const void *v, const float *rpb
  * out is its float32 output and dout is float32 [B, heads, H, W, d].
  *
  * `workspace` is caller-owned device memory of na2d_backward_workspace_bytes
- * bytes (8 per query, 16-byte aligned): the first kernel leaves each query's
- * softmax statistics there for the second, so no k*k attention tensor is
- * stored.  d must be 16, 32, 64 or 128 and ksize <= NA2D_VALU_MAX_KSIZE.
- * The gradient of the bias table is accumulated with float atomics, so its
- * last bits may differ from call to call; everything else is deterministic.
+ * bytes (16-byte aligned, contents ignored on entry): the first kernel leaves
+ * each query's softmax statistics there for the second (8 bytes per query),
+ * so no k*k attention tensor is stored, followed by per-tile partial sums of
+ * the bias gradient ((2k-1)^2 floats per 8 x 8 query tile).  d must be 16,
+ * 32, 64 or 128 and ksize <= NA2D_VALU_MAX_KSIZE.  The gradient of the bias
+ * table is summed with float atomics, so its last bits may differ from call
+ * to call; everything else is deterministic.
  * No output may overlap an input or another output.  Other conventions as
  * for na2d_forward.
  * ------------------------------------------------------------------------ */
@@ -192,8 +194,9 @@ int na2d_backward(const void *q, const void *k, const void *v, const float *rpb,
                   float *drpb, void *workspace, int B, int heads, int H, int W, int d,
                   int ksize, int dtype, void *stream);
 
-/* Bytes of workspace na2d_backward needs (0 if the sizes are invalid). */
-long long na2d_backward_workspace_bytes(int B, int heads, int H, int W);
+/* Bytes of workspace na2d_backward needs for these sizes and window (0 if
+ * they are invalid). */
+long long na2d_backward_workspace_bytes(int B, int heads, int H, int W, int ksize);
 
 /* Host-only check of na2d_backward's arguments (no HIP call). */
 int na2d_backward_check_args(const void *q, const void *k, const void *v, const float *rpb,

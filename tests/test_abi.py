@@ -217,8 +217,12 @@ def test_backward_args():
     assert check_bwd(dq=Q) == na2d.NA2D_ERR_ALIAS             # output on an input
     assert check_bwd(dk=DQ + 64) == na2d.NA2D_ERR_ALIAS       # two outputs overlap
     assert check_bwd(ws=DOUT + 16) == na2d.NA2D_ERR_ALIAS
-    assert na2d.na2d_backward_workspace_bytes(2, 2, 14, 15) == 2 * 2 * 14 * 15 * 8
-    assert na2d.na2d_backward_workspace_bytes(0, 2, 14, 15) == 0
+    assert check_bwd(ws=DOUT - 4096) == na2d.NA2D_ERR_ALIAS   # the bias-gradient tables reach dout
+    # statistics (8 bytes a query, padded to 256) then a (2k-1)^2 table per 8 x 8 tile
+    stats = (2 * 2 * 14 * 15 * 8 + 255) // 256 * 256
+    assert na2d.na2d_backward_workspace_bytes(2, 2, 14, 15, 5) == stats + 2 * 2 * 2 * 2 * 81 * 4
+    assert na2d.na2d_backward_workspace_bytes(0, 2, 14, 15, 5) == 0
+    assert na2d.na2d_backward_workspace_bytes(2, 2, 14, 15, 0) == 0
     st = na2d.na2d_backward(Q, K, V, RPB, OUT, DOUT, DQ, DK, DV, DRPB, WS, 2, 2, 14, 15, 32, 17,
                             na2d.NA2D_F16, None)
     assert st == na2d.NA2D_ERR_KSIZE                          # rejected before any launch

@@ -230,7 +230,8 @@ int check_backward(const void *q, const void *k, const void *v, const float *rpb
     for (const void *p : ptrs)
         if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return NA2D_ERR_ALIGN;
     const uint64_t queries = (uint64_t)B * heads * H * W, elems = queries * d;
-    const uint64_t in_b = elems * elem_size(dtype), f_b = elems * 4, ws_b = queries * 8;
+    const uint64_t in_b = elems * elem_size(dtype), f_b = elems * 4;
+    const uint64_t ws_b = na2d::bwd_workspace_bytes(B, heads, H, W, ksize);
     const uint64_t rpb_b = (uint64_t)heads * (2 * ksize - 1) * (2 * ksize - 1) * 4;
     struct Span { const void *p; uint64_t n; };
     const Span outs[5] = {{dq, f_b}, {dk, f_b}, {dv, f_b}, {drpb, rpb_b}, {ws, ws_b}};
@@ -257,10 +258,11 @@ extern "C" int na2d_backward_check_args(const void *q, const void *k, const void
                           d, ksize, dtype);
 }
 
-extern "C" long long na2d_backward_workspace_bytes(int B, int heads, int H, int W)
+extern "C" long long na2d_backward_workspace_bytes(int B, int heads, int H, int W, int ksize)
 {
-    if (B <= 0 || heads <= 0 || H <= 0 || W <= 0) return 0;
-    return (long long)B * heads * H * W * 8;
+    if (B <= 0 || heads <= 0 || H <= 0 || W <= 0 || ksize < 1 || ksize > NA2D_VALU_MAX_KSIZE)
+        return 0;
+    return (long long)na2d::bwd_workspace_bytes(B, heads, H, W, ksize);
 }
 
 extern "C" int na2d_backward(const void *q, const void *k, const void *v, const float *rpb,

@@ -269,18 +269,15 @@ hipError_t launch_bwd_typed(const BwdProblem &p, hipStream_t stream)
     const uint64_t blocks = (uint64_t)p.B * p.heads * a.blocks_per_map;
     if (blocks == 0 || xcd_grid(blocks) > 0x7fffffffull) return hipErrorInvalidConfiguration;
     a.nblocks = (unsigned)blocks;
+    // both passes run on the matrix cores where they apply
+    if (!std::is_same<T, float>::value && D == 32 && p.ksize <= NA2D_BWD_MFMA_MAX_KSIZE)
+        return launch_backward_mfma(p, stream);
     if (p.drpb) {  // the bias gradient accumulates: clear it first (a kernel, not a memset)
         const int n = p.heads * (2 * p.ksize - 1) * (2 * p.ksize - 1);
         hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p.drpb, n);
     }
     const dim3 grid((unsigned)xcd_grid(blocks));
     hipLaunchKernelGGL((bwd_query_kernel<T, D>), grid, dim3(kThreadsB), 0, stream, a);
-    // the key pass runs on the matrix cores where they apply
-    if (!std::is_same<T, float>::value && D == 32 && p.ksize <= NA2D_BWD_MFMA_MAX_KSIZE) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_backward_kv_mfma(p, stream);
-    }
     hipLaunchKernelGGL((bwd_key_kernel<T, D>), grid, dim3(kThreadsB), 0, stream, a);
     return hipGetLastError();
 }

@@ -97,7 +97,9 @@ struct BArgs {
     const float *rpb, *out, *dout;
     float *dq, *dk, *dv, *drpb;
     float2 *ws;
-    int heads, H, W, ks;
+    float *part;  // per-tile bias-gradient tables, (2k-1)^2 floats each
+    int B, heads, H, W, ks;
+    unsigned red_jobs;  // bias-table reduction jobs (see reduce_bias_tables)
     int tiles_x, tiles_per_map;
     unsigned ntiles;
     float c, scale;
@@ -137,6 +139,262 @@ __device__ inline u32x4 load_slice(__amdgpu_buffer_rsrc_t r, int y, int x, int W
         r, x < W ? (unsigned)(y * W + x) * 64u + 16u * (unsigned)g : kOutOfRange, 0, 0);
 }
 
+// Walks the 16-wide column blocks of rows y0..y1 (nblk a row from column x0)
+// one ahead: (ny, nxb) is the next block; past the last it stays on the last
+// row (a spare in-range load).
+struct BlockWalk {
+    int ny, nxb, b;
+    const int y1, x0, nblk;
+    __device__ BlockWalk(int y0_, int y1_, int x0_, int nblk_)
+        : ny(y0_), nxb(x0_), b(0), y1(y1_), x0(x0_), nblk(nblk_) {}
+    __device__ void advance()
+    {
+        if (++b == nblk) {
+            b = 0;
+            ny = min(ny + 1, y1);
+        }
+        nxb = x0 + 16 * b;
+    }
+};
+
+// Runs body(data, y, xb) over the blocks of `bw` in order, each block's data
+// (load(y, xb)) loaded one block ahead of its use into one of two register
+// sets taken in turn, so no copy waits on a load in flight.  Past the last
+// block the walk stays in range, so the spare loads are harmless.
+template <typename Load, typename Body>
+__device__ inline void pipelined_walk(BlockWalk bw, int nblocks, Load load, Body body)
+{
+    int ya = bw.ny, xa = bw.nxb;
+    auto sa = load(ya, xa);
+    bw.advance();
+    for (int j = 0; j + 1 < nblocks; j += 2) {
+        const int yb = bw.ny, xb = bw.nxb;
+        const auto sb = load(yb, xb);
+        bw.advance();
+        body(sa, ya, xa);
+        ya = bw.ny;
+        xa = bw.nxb;
+        sa = load(ya, xa);
+        bw.advance();
+        body(sb, yb, xb);
+    }
+    if (nblocks & 1) body(sa, ya, xa);
+}
+
+// The per-block bias gradient.  Lane (g, c) holds dS of query c (row c >> 3,
+// column c & 7 of the wave's 2 x 8 queries) against keys 4g..4g+3 of the
+// block, and the bias entry of a pair depends on (key row - query row,
+// key column - query column): within a query row the entries are the
+// diagonals of the 8 x 16 (query, key) block, which several lanes share.  The
+// block is staged in LDS and each of 2 x 23 lanes sums one diagonal, so one
+// conflict-free LDS atomic per block adds it to the workgroup's table.
+// dy0 = key row - first query row, dx0 = first key column - first query column.
+constexpr int kDsRow = 16 + 4;              // a query's 16 keys (+ padding)
+constexpr int kDsRows = 16;                 // 2 x 8 queries
+constexpr int kDiag = 23;                   // key - query column: -7..15
+constexpr int kRedRows = 32;                // tiles per workgroup of the bias reduction
+
+__device__ inline void add_bias_grad(const floatx4 &db, float *buf, float *dbias, int lane, int g,
+                                     int c, int dy0, int dx0, int ks, float scale)
+{
+    *reinterpret_cast<floatx4 *>(buf + c * kDsRow + 4 * g) = db;
+    if (lane < 2 * kDiag) {
+        const int hq = lane >= kDiag, dl = lane - kDiag * hq - 7;  // dl = key col - query col in the block
+        float sum = 0.f;
+#pragma unroll
+        for (int c7 = 0; c7 < 8; ++c7) {
+            const int kc = dl + c7;
+            if ((unsigned)kc < 16u) sum += buf[(8 * hq + c7) * kDsRow + kc];
+        }
+        const int nb = 2 * ks - 1;
+        const int row = dy0 - hq + ks - 1, col = dx0 + dl + ks - 1;
+        if (sum != 0.f && (unsigned)row < (unsigned)nb && (unsigned)col < (unsigned)nb)
+            atomicAdd(&dbias[row * nb + col], sum * scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Query pass: softmax statistics, g . o, dq and the bias gradient of 16 own
+// queries per wave, from the key blocks that their windows touch.  Writes the
+// per-query (log2-sum-exp, g . o) pair the key pass reads.
+template <typename T>
+__global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
+{
+    using FragT = typename Frag<T>::type;
+    __shared__ float raw[kBMaxRaw];
+    __shared__ float dbias[kBMaxRaw];                             // the workgroup's bias gradient
+    __shared__ __align__(16) unsigned char kbuf[kBW][16 * 64];    // streamed k block [pos][d], 16-bit
+    __shared__ __align__(16) float dsbuf[kBW][kDsRows * kDsRow];  // a block's dS by (query, key)
+    const unsigned tile = xcd_tile(blockIdx.x, gridDim.x);
+    if (tile >= a.ntiles) return;
+    const Patch P = patch_of(a, tile);
+    const int H = a.H, W = a.W, ks = a.ks, nb = 2 * ks - 1;
+    stage_raw_bias(a, P.h, raw);
+    if (a.drpb) {
+        for (int e = threadIdx.x; e < nb * nb; e += kBT) dbias[e] = 0.f;
+        // the key pass, which runs after this kernel, adds the tables into drpb
+        if (tile == 0)
+            for (int e = threadIdx.x; e < a.heads * nb * nb; e += kBT) a.drpb[e] = 0.f;
+    }
+    __syncthreads();
+
+    // the wave index is uniform: in a scalar register, loop bounds built on it stay scalar
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int qy1 = P.y0 + 2 * wave;  // the wave's query rows qy1, qy1 + 1
+    if (qy1 < H) {
+        const int qy = min(qy1 + (c >> 3), H - 1), qx = min(P.x0 + (c & 7), W - 1);
+        const bool own_valid = qy1 + (c >> 3) < H && P.x0 + (c & 7) < W;
+        const int sy = wstart(qy, ks, H), sx = wstart(qx, ks, W);
+        const unsigned map_bytes = (unsigned)H * W * 64u;
+        const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, P.base, 64, map_bytes);
+        const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, P.base, 64, map_bytes);
+        const int64_t qi = P.base + (int64_t)qy * W + qx;
+        // the wave's own queries as B operands: lane (g, c) holds slice g of query c
+        const FragT qf = __builtin_bit_cast(
+            FragT, *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + qi * 32 + 8 * g));
+        FragT gh, gl;
+        float go = 0.f;  // this lane's share of g . o
+        {
+            const float *gp = a.dout + qi * 32 + 8 * g, *op = a.out + qi * 32 + 8 * g;
+            const floatx4 g0 = *reinterpret_cast<const floatx4 *>(gp);
+            const floatx4 g1 = *reinterpret_cast<const floatx4 *>(gp + 4);
+            const floatx4 o0 = *reinterpret_cast<const floatx4 *>(op);
+            const floatx4 o1 = *reinterpret_cast<const floatx4 *>(op + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                T h, l;
+                split<T>(g0[e], h, l);
+                gh[e] = h;
+                gl[e] = l;
+                split<T>(g1[e], h, l);
+                gh[4 + e] = h;
+                gl[4 + e] = l;
+                go = fmaf(g0[e], o0[e], go);
+                go = fmaf(g1[e], o1[e], go);
+            }
+        }
+        const float dd = quad_sum(go);
+
+        // keys the wave's windows touch: rows kylo..kyhi, 16-wide column blocks from kxlo
+        const int kylo = wstart(qy1, ks, H), kyhi = wstart(min(qy1 + 1, H - 1), ks, H) + ks - 1;
+        const int kxlo = wstart(P.x0, ks, W), kxhi = wstart(min(P.x0 + 7, W - 1), ks, W) + ks - 1;
+        const int nblk = (kxhi - kxlo + 16) >> 4;
+        const int nblocks = (kyhi - kylo + 1) * nblk;
+
+        // pass 1: online max and sum of the log2-scaled logits, per lane over
+        // its keys 4g..4g+3 of each block, then over the four lane groups.
+        // Blocks run row by row.
+        float m = -1e30f, l = 0.f;
+        pipelined_walk(
+            BlockWalk(kylo, kyhi, kxlo, nblk), nblocks,
+            [&](int ky, int kxb) { return load_slice(rk, ky, kxb + c, W, g); },
+            [&](const u32x4 &kv, int ky, int kxb) {
+                const FragT ka = __builtin_bit_cast(FragT, kv);
+                const bool rowin = own_valid && (unsigned)(ky - sy) < (unsigned)ks;
+                const int brow = (ky - qy + ks - 1) * nb;
+                const floatx4 s = mfma16x16x32(ka, qf, floatx4{0, 0, 0, 0});
+                float t[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int kx = kxb + 4 * g + r;
+                    const bool in = rowin && (unsigned)(kx - sx) < (unsigned)ks;
+                    t[r] = in ? s[r] * a.c + raw[brow + kx - qx + ks - 1] : -INFINITY;
+                }
+                const float mn = fmaxf(fmaxf(m, fmaxf(t[0], t[1])), fmaxf(t[2], t[3]));
+                l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(t[0] - mn) +
+                    __builtin_amdgcn_exp2f(t[1] - mn) + __builtin_amdgcn_exp2f(t[2] - mn) +
+                    __builtin_amdgcn_exp2f(t[3] - mn);
+                m = mn;
+            });
+        const float mq = quad_max(m);
+        const float lq = quad_sum(l * __builtin_amdgcn_exp2f(m - mq));
+        const float lse = own_valid ? mq + __builtin_amdgcn_logf(lq) : 0.f;
+
+        // pass 2: P, dS, dq^T += k^T dS^T and the bias gradient
+        floatx4 dq[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
+        floatx4 dql[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
+        unsigned char *kb = kbuf[wave];
+        const unsigned tr_off = (unsigned)(4 * g + (c >> 2)) * 64u + 8u * (unsigned)(c & 3);
+        struct KV {
+            u32x4 k, v;
+        };
+        pipelined_walk(
+            BlockWalk(kylo, kyhi, kxlo, nblk), nblocks,
+            [&](int ky, int kxb) {
+                return KV{load_slice(rk, ky, kxb + c, W, g), load_slice(rv, ky, kxb + c, W, g)};
+            },
+            [&](const KV &blk, int ky, int kxb) {
+                const u32x4 kv = blk.k, vv = blk.v;
+                const bool rowin = own_valid && (unsigned)(ky - sy) < (unsigned)ks;
+                const int brow = (ky - qy + ks - 1) * nb;
+                *reinterpret_cast<u32x4 *>(kb + (unsigned)c * 64u + 16u * g) = kv;
+                const FragT ka = __builtin_bit_cast(FragT, kv), va = __builtin_bit_cast(FragT, vv);
+                const floatx4 s = mfma16x16x32(ka, qf, floatx4{0, 0, 0, 0});
+                const floatx4 gvh = mfma16x16x32(va, gh, floatx4{0, 0, 0, 0});
+                const floatx4 gvl = mfma16x16x32(va, gl, floatx4{0, 0, 0, 0});
+                const floatx4 gv = gvh + gvl * LoScale<T>::down;
+                v4i16 sh, sl;
+                floatx4 db;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int kx = kxb + 4 * g + r;
+                    const bool in = rowin && (unsigned)(kx - sx) < (unsigned)ks;
+                    const float p = in ? __builtin_amdgcn_exp2f(s[r] * a.c + raw[in ? brow + kx - qx + ks - 1 : 0] - lse) : 0.f;
+                    const float ds = p * (gv[r] - dd);
+                    db[r] = ds;
+                    T h, lo;
+                    split<T>(ds, h, lo);
+                    sh[r] = bits(h);
+                    sl[r] = bits(lo);
+                }
+                if (a.drpb) add_bias_grad(db, dsbuf[wave], dbias, lane, g, c, ky - qy1, kxb - P.x0, ks, a.scale);
+#pragma unroll
+                for (int dh = 0; dh < 2; ++dh) {
+                    const v4i16 kt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(kb + tr_off + 32u * dh));
+                    dq[dh] = mfma16x16x16(kt, sh, dq[dh], T{});
+                    dql[dh] = mfma16x16x16(kt, sl, dql[dh], T{});
+                }
+            });
+        // lane (g, c): dims 16 dh + 4 g + j of query c
+        if (own_valid) {
+            if (g == 0) a.ws[qi] = make_float2(lse, dd);
+#pragma unroll
+            for (int dh = 0; dh < 2; ++dh)
+                *reinterpret_cast<floatx4 *>(a.dq + qi * 32 + 16 * dh + 4 * g) =
+                    (dq[dh] + dql[dh] * LoScale<T>::down) * a.scale;
+        }
+    }
+    if (a.drpb) {  // the tile's table, summed over tiles by reduce_bias_tables
+        __syncthreads();
+        float *dst = a.part + (int64_t)tile * nb * nb;
+        for (int e = threadIdx.x; e < nb * nb; e += kBT) dst[e] = dbias[e];
+    }
+}
+
+// drpb[h] += the tables of tiles [chunk * kRedRows, ...) of head h, for
+// job = chunk * heads + h (tiles are numbered map-major, map = b * heads + h).
+// Run by the first workgroups of the key pass, after the query pass wrote the
+// tables and cleared drpb.
+__device__ inline void reduce_bias_tables(const BArgs &a, unsigned job)
+{
+    const int nbb = (2 * a.ks - 1) * (2 * a.ks - 1);
+    const int h = job % a.heads, chunk = job / a.heads;
+    const int rows = a.B * a.tiles_per_map;
+    const int r0 = chunk * kRedRows;
+    for (int e = threadIdx.x; e < nbb; e += kBT) {
+        float acc = 0.f;
+#pragma unroll 8
+        for (int i = 0; i < kRedRows; ++i) {
+            const int r = min(r0 + i, rows - 1);  // a row past the end is read but not added
+            const int b = r / a.tiles_per_map, t = r - b * a.tiles_per_map;
+            const float v = a.part[((int64_t)(b * a.heads + h) * a.tiles_per_map + t) * nbb + e];
+            acc += r0 + i < rows ? v : 0.f;
+        }
+        unsafeAtomicAdd(&a.drpb[(int64_t)h * nbb + e], acc);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Key pass: dk, dv of 16 own keys per wave from every query holding them.
 template <typename T>
@@ -146,13 +404,15 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
     __shared__ float raw[kBMaxRaw];
     __shared__ __align__(16) unsigned char qbuf[kBW][16 * 64];    // streamed q block [pos][d], 16-bit
     __shared__ __align__(16) unsigned char gbuf[kBW][2][16 * 64]; // streamed g block, hi and lo
+    if (a.drpb && blockIdx.x < a.red_jobs) reduce_bias_tables(a, blockIdx.x);
     const unsigned tile = xcd_tile(blockIdx.x, gridDim.x);
     if (tile >= a.ntiles) return;
     const Patch P = patch_of(a, tile);
     stage_raw_bias(a, P.h, raw);
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is uniform: in a scalar register, loop bounds built on it stay scalar
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
     const int H = a.H, W = a.W, ks = a.ks, nb = 2 * ks - 1;
     const int ky1 = P.y0 + 2 * wave;                 // the wave's key rows ky1, ky1 + 1
@@ -189,19 +449,26 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
     // position 4 g + (i >> 2) and receives dim 16 dh + i of positions 4 g .. 4 g + 3
     const unsigned tr_off = (unsigned)(4 * g + (c >> 2)) * 64u + 8u * (unsigned)(c & 3);
 
-    for (int y = ylo; y <= yhi; ++y) {
-        const int sy = wstart(y, ks, H);
-        for (int b = 0; b < nblk; ++b) {
-            const int xb = xlo + 16 * b;
-            // streamed block: q and g rows of queries (y, xb + i)
-            const u32x4 qv = load_slice(rq, y, xb + c, W, g);
-            const unsigned goff = xb + c < W ? (unsigned)(y * W + xb + c) * 128u + 32u * g : kOutOfRange;
-            const u32x4 g0 = __builtin_amdgcn_raw_buffer_load_b128(rg, goff, 0, 0);
-            const u32x4 g1 = __builtin_amdgcn_raw_buffer_load_b128(rg, goff + 16u, 0, 0);
-            // softmax statistics of queries xb + 4 g + r (r = 0..3), zeros past the map
-            const unsigned woff = xb + 4 * g < W ? (unsigned)(y * W + xb + 4 * g) * 8u : kOutOfRange;
-            const u32x4 w01 = __builtin_amdgcn_raw_buffer_load_b128(rw, woff, 0, 0);
-            const u32x4 w23 = __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 16u, 0, 0);
+    // streamed block at (y, xb): q and g rows of queries (y, xb + i), and the
+    // softmax statistics of queries xb + 4 g + r (r = 0..3); zeros past the map
+    struct Streamed {
+        u32x4 q, g0, g1, w01, w23;
+    };
+    auto load_block = [&](int y, int xb) {
+        Streamed t;
+        t.q = load_slice(rq, y, xb + c, W, g);
+        const unsigned goff = xb + c < W ? (unsigned)(y * W + xb + c) * 128u + 32u * g : kOutOfRange;
+        t.g0 = __builtin_amdgcn_raw_buffer_load_b128(rg, goff, 0, 0);
+        t.g1 = __builtin_amdgcn_raw_buffer_load_b128(rg, goff + 16u, 0, 0);
+        const unsigned woff = xb + 4 * g < W ? (unsigned)(y * W + xb + 4 * g) * 8u : kOutOfRange;
+        t.w01 = __builtin_amdgcn_raw_buffer_load_b128(rw, woff, 0, 0);
+        t.w23 = __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 16u, 0, 0);
+        return t;
+    };
+    auto process = [&](const Streamed &cur, int y, int xb) {
+        {
+            const int sy = wstart(y, ks, H);
+            const u32x4 qv = cur.q, g0 = cur.g0, g1 = cur.g1, w01 = cur.w01, w23 = cur.w23;
             // q as A operand (the block's positions as rows), its copy for q^T
             *reinterpret_cast<u32x4 *>(qb + (unsigned)c * 64u + 16u * g) = qv;
             FragT gh, gl;
@@ -261,7 +528,9 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
                 dkl[dh] = mfma16x16x16(qt, sl, dkl[dh], T{});
             }
         }
-    }
+    };
+    // blocks row by row
+    pipelined_walk(BlockWalk(ylo, yhi, xlo, nblk), (yhi - ylo + 1) * nblk, load_block, process);
     // lane (g, c): dims 16 dh + 4 g + j of key c
     if (own_valid) {
         const int64_t kj = P.base + (int64_t)ky * W + kx;
@@ -277,9 +546,10 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
 
 }  // namespace
 
-// Gradients with the key pass on the matrix cores; the query pass (dq, the
-// bias gradient and the workspace) is run by `query_pass` first.
-hipError_t launch_backward_kv_mfma(const BwdProblem &p, hipStream_t stream)
+// Both passes on the matrix cores: the query pass (dq, the bias gradient and
+// the per-query statistics), then the key pass that reads those statistics.
+// The bias gradient must already be cleared.
+hipError_t launch_backward_mfma(const BwdProblem &p, hipStream_t stream)
 {
     BArgs a;
     a.q = p.q;
@@ -293,6 +563,9 @@ hipError_t launch_backward_kv_mfma(const BwdProblem &p, hipStream_t stream)
     a.dv = p.dv;
     a.drpb = p.drpb;
     a.ws = reinterpret_cast<float2 *>(p.workspace);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(p.workspace) +
+                                       bwd_stats_bytes(p.B, p.heads, p.H, p.W));
+    a.B = p.B;
     a.heads = p.heads;
     a.H = p.H;
     a.W = p.W;
@@ -304,13 +577,18 @@ hipError_t launch_backward_kv_mfma(const BwdProblem &p, hipStream_t stream)
     const uint64_t tiles = (uint64_t)p.B * p.heads * a.tiles_per_map;
     if (tiles == 0 || xcd_grid(tiles) > 0x7fffffffull) return hipErrorInvalidConfiguration;
     a.ntiles = (unsigned)tiles;
+    a.red_jobs = (unsigned)(((uint64_t)p.B * a.tiles_per_map + kRedRows - 1) / kRedRows * p.heads);
     const dim3 grid((unsigned)xcd_grid(tiles));
-    if (p.dtype == NA2D_F16)
+    if (a.red_jobs > grid.x) return hipErrorInvalidConfiguration;  // cannot happen: a job spans >= 32 tiles
+    if (p.dtype == NA2D_F16) {
+        hipLaunchKernelGGL(bwd_q_mfma_kernel<_Float16>, grid, dim3(kBT), 0, stream, a);
         hipLaunchKernelGGL(bwd_kv_mfma_kernel<_Float16>, grid, dim3(kBT), 0, stream, a);
-    else if (p.dtype == NA2D_BF16)
+    } else if (p.dtype == NA2D_BF16) {
+        hipLaunchKernelGGL(bwd_q_mfma_kernel<__bf16>, grid, dim3(kBT), 0, stream, a);
         hipLaunchKernelGGL(bwd_kv_mfma_kernel<__bf16>, grid, dim3(kBT), 0, stream, a);
-    else
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -26,12 +26,29 @@ struct BwdProblem {
     int B, heads, H, W, d, ksize, dtype;
 };
 
+// The backward workspace: per query its softmax statistics (a float2), then,
+// from a 256-byte boundary, one (2k-1)^2 float table per 8 x 8 query tile
+// (the tile's share of the bias gradient, summed by a second kernel).
+inline unsigned long long bwd_stats_bytes(int B, int heads, int H, int W)
+{
+    return ((unsigned long long)B * heads * H * W * 8ull + 255ull) & ~255ull;
+}
+inline unsigned long long bwd_tiles(int B, int heads, int H, int W)
+{
+    return (unsigned long long)B * heads * ((H + 7) / 8) * ((W + 7) / 8);
+}
+inline unsigned long long bwd_workspace_bytes(int B, int heads, int H, int W, int ksize)
+{
+    const unsigned long long nb = 2ull * ksize - 1;
+    return bwd_stats_bytes(B, heads, H, W) + bwd_tiles(B, heads, H, W) * nb * nb * 4ull;
+}
+
 // Launchers; each returns the HIP status of its launch.  The arguments have
 // been checked by the caller.
 hipError_t launch_valu(const Problem &p, hipStream_t stream);
 hipError_t launch_mfma(const Problem &p, hipStream_t stream);     // square 2D windows
 hipError_t launch_mfma_1d(const Problem &p, hipStream_t stream);  // NA1D
 hipError_t launch_backward(const BwdProblem &p, hipStream_t stream);
-hipError_t launch_backward_kv_mfma(const BwdProblem &p, hipStream_t stream);  // key pass on MFMA
+hipError_t launch_backward_mfma(const BwdProblem &p, hipStream_t stream);  // both passes on MFMA
 
 }  // namespace na2d

@@ -84,7 +84,7 @@ def load() -> ctypes.CDLL:
         lib.sasa2d_forward.restype = I
         lib.na2d_backward.argtypes = [P] * 11 + [I] * 7 + [P]
         lib.na2d_backward.restype = I
-        lib.na2d_backward_workspace_bytes.argtypes = [I] * 4
+        lib.na2d_backward_workspace_bytes.argtypes = [I] * 5
         lib.na2d_backward_workspace_bytes.restype = ctypes.c_longlong
         lib.na2d_backward_check_args.argtypes = [P] * 11 + [I] * 7
         lib.na2d_backward_check_args.restype = I
@@ -162,8 +162,8 @@ def na2d_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads
                                 B, heads, H, W, d, ksize, dtype, _stream(stream))
 
 
-def na2d_backward_workspace_bytes(B, heads, H, W) -> int:
-    return load().na2d_backward_workspace_bytes(B, heads, H, W)
+def na2d_backward_workspace_bytes(B, heads, H, W, ksize) -> int:
+    return load().na2d_backward_workspace_bytes(B, heads, H, W, ksize)
 
 
 def na2d_backward_check_args(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads, H, W,
@@ -297,7 +297,7 @@ def backward(q, k, v, rpb, out, dout, ksize: int, stream=None):
     f32 = dict(dtype=torch.float32, device=q.device)
     dq, dk, dv = torch.empty(q.shape, **f32), torch.empty(q.shape, **f32), torch.empty(q.shape, **f32)
     drpb = None if rpb is None else torch.empty(rpb.shape, **f32)
-    ws = torch.empty(max(1, na2d_backward_workspace_bytes(B, heads, H, W) // 4), **f32)
+    ws = torch.empty(max(1, na2d_backward_workspace_bytes(B, heads, H, W, ksize) // 4), **f32)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = na2d_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, ws, B, heads, H, W, d, ksize,
