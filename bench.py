@@ -33,13 +33,14 @@ ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
 # kernel family -> its source (a committed traffic summary is used only when it
 # was taken on the source as it is now)
 KERNEL_SOURCES = {"na_valu": "na_valu.hip", "na2d_mfma": "na2d_mfma.hip",
-                  "na1d_mfma": "na1d_mfma.hip", "na2d_bwd": "na2d_bwd.hip"}
+                  "na1d_mfma": "na1d_mfma.hip", "na3d_mfma": "na3d_mfma.hip",
+                  "na2d_bwd": "na2d_bwd_mfma.hip"}
 
 
 def kernel_id(op: str, algo: int) -> str:
     if algo == 1:
         return "na_valu"
-    return "na1d_mfma" if op == "na1d" else "na2d_mfma"
+    return {"na1d": "na1d_mfma", "na3d": "na3d_mfma"}.get(op, "na2d_mfma")
 
 
 def algorithmic_bytes(w) -> int:
@@ -182,7 +183,10 @@ def bench_backward(args, w, wname, lib, dev, dtype_code):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic: Q,K,V ~ N(0,1), RPB ~ N(0,0.02), dout ~ N(0,1)",
         "config": {"workload": wname, "pass": "backward", "B": w.B, "heads": w.heads, "H": w.H,
-                   "W": w.W, "d": w.d, "k": w.k, "kernel": "valu", "rotating_sets": nsets,
+                   "W": w.W, "d": w.d, "k": w.k, "rotating_sets": nsets,
+                   # 16-bit inputs with d = 32 and k <= 25 run on the matrix cores
+                   "kernel": "mfma" if w.dtype != "f32" and w.d == 32 and w.k <= 25 else "valu",
+                   "roofline_scope": "whole backward (all its kernels)",
                    "algorithmic_bytes_per_step": set_bytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -263,19 +267,15 @@ def main():
     torch.cuda.set_device(dev)
     dtype_code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
     algo = ALGOS[args.algo]
-    if algo == 0:
-        # the matrix-core kernel serves square 2D windows (NA and SASA)
-        if w.op in ("na2d", "sasa2d"):
-            algo = na2d.na2d_select_algo(w.H, w.W, w.d, w.k, dtype_code)
-        elif w.op == "na1d" and w.dtype != "f32" and w.d == 32 and 3 <= w.k <= 63:
-            algo = na2d.NA2D_ALGO_MFMA
-        else:
-            algo = na2d.NA2D_ALGO_VALU
-    algo_name = {1: "valu", 2: "mfma"}[algo]
     # the grid and window of the general entry point: [B, heads, D, H, W], (kd, kh, kw)
     grid = (w.depth, w.H, w.W)
     window = {"na1d": (1, 1, w.k), "na3d": (w.k, w.k, w.k)}.get(w.op, (1, w.k, w.k))
     mode = na2d.NA_WINDOW_SASA if w.op == "sasa2d" else na2d.NA_WINDOW_NA
+    if algo == 0:  # the family the library's own automatic choice resolves to
+        algo = na2d.na_select_algo_nd(*grid, w.d, window, mode, dtype_code)
+        if algo < 0:
+            raise RuntimeError("unsupported workload: %s" % na2d.na2d_strerror(algo))
+    algo_name = {1: "valu", 2: "mfma"}[algo]
 
     if args.backward:
         if w.op != "na2d":

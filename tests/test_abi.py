@@ -95,7 +95,7 @@ def test_unsupported():
     assert check(d=48) == na2d.NA2D_ERR_UNSUPPORTED                  # no kernel for d = 48
     assert check(d=64, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED
     assert check(dtype=na2d.NA2D_F32, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED
-    assert check(ksize=1, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED
+    assert check(ksize=1, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_OK  # the general kernel
     big = dict(H=64, W=64, ksize=27)
     assert check(algo=na2d.NA2D_ALGO_MFMA, **big) == na2d.NA2D_ERR_UNSUPPORTED
     assert check(**big) == na2d.NA2D_OK                              # AUTO falls back to VALU
@@ -129,7 +129,20 @@ def test_select_algo():
     assert na2d.na2d_select_algo(56, 56, 32, 7, na2d.NA2D_F16) == na2d.NA2D_ALGO_MFMA
     assert na2d.na2d_select_algo(128, 128, 32, 21, na2d.NA2D_BF16) == na2d.NA2D_ALGO_MFMA
     assert na2d.na2d_select_algo(14, 14, 32, 7, na2d.NA2D_F32) == na2d.NA2D_ALGO_VALU
-    assert na2d.na2d_select_algo(14, 14, 32, 1, na2d.NA2D_F16) == na2d.NA2D_ALGO_VALU
+    # a window of 1 is served by the general matrix-core kernel
+    assert na2d.na2d_select_algo(14, 14, 32, 1, na2d.NA2D_F16) == na2d.NA2D_ALGO_MFMA
+    assert na2d.na2d_select_algo(14, 14, 64, 7, na2d.NA2D_F16) == na2d.NA2D_ALGO_VALU
+    NA, SASA = na2d.NA_WINDOW_NA, na2d.NA_WINDOW_SASA
+    f16 = na2d.NA2D_F16
+    assert na2d.na_select_algo_nd(16, 56, 56, 32, (5, 5, 5), NA, f16) == na2d.NA2D_ALGO_MFMA
+    assert na2d.na_select_algo_nd(16, 56, 56, 32, (11, 5, 5), NA, f16) == na2d.NA2D_ALGO_VALU
+    assert na2d.na_select_algo_nd(1, 20, 30, 32, (1, 3, 7), NA, f16) == na2d.NA2D_ALGO_MFMA
+    assert na2d.na_select_algo_nd(1, 20, 30, 32, (1, 3, 7), SASA, f16) == na2d.NA2D_ALGO_VALU
+    assert na2d.na_select_algo_nd(1, 20, 30, 32, (1, 7, 7), SASA, f16) == na2d.NA2D_ALGO_MFMA
+    assert na2d.na_select_algo_nd(1, 1, 3136, 32, (1, 1, 49), NA, f16) == na2d.NA2D_ALGO_MFMA
+    assert na2d.na_select_algo_nd(4, 9, 9, 32, (3, 3, 3), NA, na2d.NA2D_F32) == na2d.NA2D_ALGO_VALU
+    assert na2d.na_select_algo_nd(4, 9, 9, 32, (3, 3, 3), 7, f16) == na2d.NA2D_ERR_UNSUPPORTED
+    assert na2d.na_select_algo_nd(4, 9, 9, 32, (11, 3, 3), NA, f16) == na2d.NA2D_ERR_KSIZE
     assert na2d.na2d_select_algo(14, 14, 32, 8, na2d.NA2D_F16) == na2d.NA2D_ERR_KSIZE
 
 
@@ -169,8 +182,13 @@ def test_nd_errors():
     assert check_nd(kh=0, mode=1) == na2d.NA2D_ERR_KSIZE
     assert check_nd(D=0) == na2d.NA2D_ERR_SHAPE
     assert check_nd(kw=65, mode=1) == na2d.NA2D_ERR_UNSUPPORTED
-    assert check_nd(algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED      # 3D: VALU only
-    assert check_nd(D=1, kd=1, kh=5, kw=3, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED
+    # the general matrix-core kernel: NA windows up to 9 on every axis
+    assert check_nd(algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_OK                   # 3D
+    assert check_nd(D=1, kd=1, kh=5, kw=3, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_OK
+    assert check_nd(D=12, kd=11, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED
+    assert check_nd(D=1, kd=1, kh=5, kw=3, mode=1,
+                    algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED   # rectangular SASA
+    assert check_nd(d=64, algo=na2d.NA2D_ALGO_MFMA) == na2d.NA2D_ERR_UNSUPPORTED
     one_d = dict(D=1, H=1, W=300, kd=1, kh=1)
     assert check_nd(kw=63, algo=na2d.NA2D_ALGO_MFMA, **one_d) == na2d.NA2D_OK       # NA1D kernel
     assert check_nd(kw=65, algo=na2d.NA2D_ALGO_MFMA, **one_d) == na2d.NA2D_ERR_UNSUPPORTED

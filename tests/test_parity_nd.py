@@ -145,3 +145,30 @@ def test_na1d_both_kernels(shape, ks, dtype, algo):
     torch.cuda.synchronize()
     finish(got.reshape(shape), oracle.na1d_forward(x.q64, x.k64, x.v64, x.rpb64, ks), dtype,
            "na1d %s k=%d algo=%d" % (shape, ks, algo))
+
+
+# The matrix-core kernel for other NA windows: 3D windows (cubic or not, a
+# window of 1 on some axis) and rectangular 2D windows; ragged 8 x 8 patches,
+# windows as wide as the axis, and both odd and even counts of key blocks.
+ND_MFMA = [((2, 2, 6, 7, 9, 32), (3, 3, 3)), ((1, 2, 7, 19, 21, 32), (5, 5, 5)),
+           ((1, 1, 5, 17, 17, 32), (5, 7, 3)), ((1, 1, 9, 9, 10, 32), (9, 9, 9)),
+           ((2, 1, 3, 13, 11, 32), (1, 3, 5)), ((1, 2, 1, 23, 18, 32), (1, 3, 9)),
+           ((1, 1, 1, 12, 40, 32), (1, 9, 1)), ((1, 1, 4, 16, 16, 32), (3, 1, 1)),
+           ((1, 1, 2, 8, 8, 32), (1, 1, 1))]
+
+
+@pytest.mark.parametrize("shape,window", ND_MFMA, ids=str)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("algo", [na2d.NA2D_ALGO_VALU, na2d.NA2D_ALGO_MFMA])
+def test_nd_windows_both_kernels(shape, window, dtype, algo):
+    print("nd", shape, window, dtype, algo, flush=True)
+    kd, kh, kw = window
+    x = make_inputs(shape, 1, dtype, seed=6, op="na3d")
+    rng = np.random.default_rng(7)
+    rpb = rng.standard_normal((shape[1], 2 * kd - 1, 2 * kh - 1, 2 * kw - 1))
+    got = na2d.forward_nd(dev(x.q), dev(x.k), dev(x.v), torch.from_numpy(rpb.astype(np.float32)).cuda(),
+                          window, na2d.NA_WINDOW_NA, algo)
+    torch.cuda.synchronize()
+    want = oracle.default_nd().forward(x.q64, x.k64, x.v64, rpb.astype(np.float32).astype(np.float64),
+                                       window, na2d.NA_WINDOW_NA)
+    finish(got, want, dtype, "nd %s %s algo=%d" % (shape, window, algo))

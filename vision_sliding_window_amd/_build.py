@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libna2d.so")
 
-SOURCES = ["na2d_api.cpp", "na_valu.hip", "na2d_mfma.hip", "na1d_mfma.hip", "na2d_bwd.hip", "na2d_bwd_mfma.hip"]
+SOURCES = ["na2d_api.cpp", "na_valu.hip", "na2d_mfma.hip", "na1d_mfma.hip", "na2d_bwd.hip", "na2d_bwd_mfma.hip",
+           "na3d_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -50,10 +50,19 @@ bool is_mfma_2d(const Nd &n)
 
 // Both take 16-bit inputs with d = 32 and address one (b, h) map with 32-bit
 // byte offsets.
+// Any other NA window with every axis small enough: 3D windows and the
+// rectangular 2D ones.
+bool is_mfma_3d(const Nd &n)
+{
+    return !is_mfma_1d(n) && !is_mfma_2d(n) && n.mode == NA_WINDOW_NA &&
+           n.kd <= NA3D_MFMA_MAX_KSIZE && n.kh <= NA3D_MFMA_MAX_KSIZE && n.kw <= NA3D_MFMA_MAX_KSIZE;
+}
+
 bool mfma_supports(const Nd &n, int dtype)
 {
     return (dtype == NA2D_F16 || dtype == NA2D_BF16) && n.d == 32 &&
-           (is_mfma_1d(n) || is_mfma_2d(n)) && (uint64_t)n.H * n.W * n.d * 4 <= 0x7fffffffull;
+           (is_mfma_1d(n) || is_mfma_2d(n) || is_mfma_3d(n)) &&
+           (uint64_t)n.D * n.H * n.W * n.d * 4 <= 0x7fffffffull;
 }
 
 bool window_ok(int k, int L, int mode)
@@ -121,7 +130,9 @@ int forward_nd(const void *q, const void *k, const void *v, const float *rpb, fl
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (resolve_algo(n, dtype, algo) == NA2D_ALGO_MFMA)
-        e = is_mfma_1d(n) ? na2d::launch_mfma_1d(p, s) : na2d::launch_mfma(p, s);
+        e = is_mfma_1d(n)   ? na2d::launch_mfma_1d(p, s)
+            : is_mfma_2d(n) ? na2d::launch_mfma(p, s)
+                            : na2d::launch_mfma_3d(p, s);
     else
         e = na2d::launch_valu(p, s);
     if (e != hipSuccess) {
@@ -150,6 +161,19 @@ extern "C" int na2d_select_algo(int H, int W, int d, int ksize, int dtype)
 {
     if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
     const Nd n = nd_2d(1, 1, H, W, d, ksize, NA_WINDOW_NA);
+    const int st = check_sizes(n);
+    if (st != NA2D_OK) return st;
+    const int a = resolve_algo(n, dtype, NA2D_ALGO_AUTO);
+    if (a == NA2D_ALGO_VALU && !valu_supports(n)) return NA2D_ERR_UNSUPPORTED;
+    return a;
+}
+
+extern "C" int na_select_algo_nd(int D, int H, int W, int d, int kd, int kh, int kw, int mode,
+                                 int dtype)
+{
+    if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
+    if (mode != NA_WINDOW_NA && mode != NA_WINDOW_SASA) return NA2D_ERR_UNSUPPORTED;
+    const Nd n{1, 1, D, H, W, d, kd, kh, kw, mode};
     const int st = check_sizes(n);
     if (st != NA2D_OK) return st;
     const int a = resolve_algo(n, dtype, NA2D_ALGO_AUTO);

@@ -84,6 +84,16 @@ __device__ inline int wstart(int i, int ks, int L)
     return s > L - ks ? L - ks : s;
 }
 
+// Entry i of the LDS bias table, read whether or not the caller will use it
+// (i clamped into the table): the empty asm keeps the read out of a branch
+// on the caller's mask, so the reads of a block issue together.
+__device__ inline float table_at(const float *raw, int i, int n)
+{
+    float b = raw[min(max(i, 0), n - 1)];
+    asm volatile("" : "+v"(b));
+    return b;
+}
+
 // positions of an axis whose window holds j (see na2d_bwd.hip)
 __device__ inline void holders(int j, int ks, int L, int &lo, int &hi)
 {
@@ -204,7 +214,9 @@ __device__ inline void add_bias_grad(const floatx4 &db, float *buf, float *dbias
 #pragma unroll
         for (int c7 = 0; c7 < 8; ++c7) {
             const int kc = dl + c7;
-            if ((unsigned)kc < 16u) sum += buf[(8 * hq + c7) * kDsRow + kc];
+            float v = buf[(8 * hq + c7) * kDsRow + min(max(kc, 0), 15)];
+            asm volatile("" : "+v"(v));  // read on every lane, no branch
+            sum += (unsigned)kc < 16u ? v : 0.f;
         }
         const int nb = 2 * ks - 1;
         const int row = dy0 - hq + ks - 1, col = dx0 + dl + ks - 1;
@@ -299,7 +311,8 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
                 for (int r = 0; r < 4; ++r) {
                     const int kx = kxb + 4 * g + r;
                     const bool in = rowin && (unsigned)(kx - sx) < (unsigned)ks;
-                    t[r] = in ? s[r] * a.c + raw[brow + kx - qx + ks - 1] : -INFINITY;
+                    const float b = table_at(raw, brow + kx - qx + ks - 1, nb * nb);
+                    t[r] = in ? s[r] * a.c + b : -INFINITY;
                 }
                 const float mn = fmaxf(fmaxf(m, fmaxf(t[0], t[1])), fmaxf(t[2], t[3]));
                 l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(t[0] - mn) +
@@ -340,7 +353,8 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
                 for (int r = 0; r < 4; ++r) {
                     const int kx = kxb + 4 * g + r;
                     const bool in = rowin && (unsigned)(kx - sx) < (unsigned)ks;
-                    const float p = in ? __builtin_amdgcn_exp2f(s[r] * a.c + raw[in ? brow + kx - qx + ks - 1 : 0] - lse) : 0.f;
+                    const float b = table_at(raw, brow + kx - qx + ks - 1, nb * nb);
+                    const float p = in ? __builtin_amdgcn_exp2f(s[r] * a.c + b - lse) : 0.f;
                     const float ds = p * (gv[r] - dd);
                     db[r] = ds;
                     T h, lo;
@@ -504,7 +518,7 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
                 const int x = xb + 4 * g + r;
                 const bool in = rowin && x < W && (unsigned)(kx - wstart(min(x, W - 1), ks, W)) < (unsigned)ks;
                 // key inside the query's window: the offset indexes the table
-                const float bias = raw[in ? (ky - y + ks - 1) * nb + (kx - x + ks - 1) : 0];
+                const float bias = table_at(raw, (ky - y + ks - 1) * nb + (kx - x + ks - 1), nb * nb);
                 const float p = in ? __builtin_amdgcn_exp2f(s[r] * a.c + bias - lse[r]) : 0.f;
                 const float ds = p * (gv[r] - dd[r]);
                 T h, l;

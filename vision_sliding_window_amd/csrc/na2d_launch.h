@@ -48,6 +48,7 @@ inline unsigned long long bwd_workspace_bytes(int B, int heads, int H, int W, in
 hipError_t launch_valu(const Problem &p, hipStream_t stream);
 hipError_t launch_mfma(const Problem &p, hipStream_t stream);     // square 2D windows
 hipError_t launch_mfma_1d(const Problem &p, hipStream_t stream);  // NA1D
+hipError_t launch_mfma_3d(const Problem &p, hipStream_t stream);  // other NA windows (3D, rectangular 2D)
 hipError_t launch_backward(const BwdProblem &p, hipStream_t stream);
 hipError_t launch_backward_mfma(const BwdProblem &p, hipStream_t stream);  // both passes on MFMA
 

@@ -31,6 +31,7 @@ NA2D_ERR_HIP = -8
 NA2D_ERR_ALGO = -9
 
 EXPORTS = ["na2d_forward", "na2d_forward_ex", "na2d_check_args", "na2d_select_algo",
+           "na_select_algo_nd",
            "na2d_strerror", "na2d_last_error", "na2d_version", "na_forward_nd",
            "na_check_args_nd", "na1d_forward", "na3d_forward", "sasa2d_forward",
            "na2d_backward", "na2d_backward_workspace_bytes", "na2d_backward_check_args"]
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
         lib.na2d_check_args.restype = I
         lib.na2d_select_algo.argtypes = [I] * 5
         lib.na2d_select_algo.restype = I
+        lib.na_select_algo_nd.argtypes = [I] * 9
+        lib.na_select_algo_nd.restype = I
         lib.na2d_strerror.argtypes = [I]
         lib.na2d_strerror.restype = ctypes.c_char_p
         lib.na2d_last_error.argtypes = []
@@ -126,6 +129,12 @@ def na2d_check_args(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, algo) ->
 
 def na2d_select_algo(H, W, d, ksize, dtype) -> int:
     return load().na2d_select_algo(H, W, d, ksize, dtype)
+
+
+def na_select_algo_nd(D, H, W, d, window, mode, dtype) -> int:
+    """The kernel family AUTO picks for na_forward_nd; window = (kd, kh, kw)."""
+    kd, kh, kw = window
+    return load().na_select_algo_nd(D, H, W, d, kd, kh, kw, mode, dtype)
 
 
 def na_forward_nd(q, k, v, rpb, out, B, heads, D, H, W, d, kd, kh, kw, mode, dtype, algo,
