@@ -328,7 +328,8 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
         floatx4 dq[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
         floatx4 dql[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
         unsigned char *kb = kbuf[wave];
-        const unsigned tr_off = (unsigned)(4 * g + (c >> 2)) * 64u + 8u * (unsigned)(c & 3);
+        const unsigned tr_off0 = tr_read_off(g, c, 0), tr_off1 = tr_read_off(g, c, 1);
+        const unsigned st_off = stage_off(g, c);
         struct KV {
             u32x4 k, v;
         };
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
                 const u32x4 kv = blk.k, vv = blk.v;
                 const bool rowin = own_valid && (unsigned)(ky - sy) < (unsigned)ks;
                 const int brow = (ky - qy + ks - 1) * nb;
-                *reinterpret_cast<u32x4 *>(kb + (unsigned)c * 64u + 16u * g) = kv;
+                *reinterpret_cast<u32x4 *>(kb + st_off) = kv;
                 const FragT ka = __builtin_bit_cast(FragT, kv), va = __builtin_bit_cast(FragT, vv);
                 const floatx4 s = mfma16x16x32(ka, qf, floatx4{0, 0, 0, 0});
                 const floatx4 gvh = mfma16x16x32(va, gh, floatx4{0, 0, 0, 0});
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
                 if (a.drpb) add_bias_grad(db, dsbuf[wave], dbias, lane, g, c, ky - qy1, kxb - P.x0, ks, a.scale);
 #pragma unroll
                 for (int dh = 0; dh < 2; ++dh) {
-                    const v4i16 kt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(kb + tr_off + 32u * dh));
+                    const v4i16 kt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(kb + (dh ? tr_off1 : tr_off0)));
                     dq[dh] = mfma16x16x16(kt, sh, dq[dh], T{});
                     dql[dh] = mfma16x16x16(kt, sl, dql[dh], T{});
                 }
@@ -461,7 +462,8 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
     unsigned char *gbh = gbuf[wave][0], *gbl = gbuf[wave][1];
     // transposed reads: lane (g, i) takes dims 16 dh + 4 (i & 3) .. + 3 of
     // position 4 g + (i >> 2) and receives dim 16 dh + i of positions 4 g .. 4 g + 3
-    const unsigned tr_off = (unsigned)(4 * g + (c >> 2)) * 64u + 8u * (unsigned)(c & 3);
+    const unsigned tr_off0 = tr_read_off(g, c, 0), tr_off1 = tr_read_off(g, c, 1);
+    const unsigned st_off = stage_off(g, c);
 
     // streamed block at (y, xb): q and g rows of queries (y, xb + i), and the
     // softmax statistics of queries xb + 4 g + r (r = 0..3); zeros past the map
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
             const int sy = wstart(y, ks, H);
             const u32x4 qv = cur.q, g0 = cur.g0, g1 = cur.g1, w01 = cur.w01, w23 = cur.w23;
             // q as A operand (the block's positions as rows), its copy for q^T
-            *reinterpret_cast<u32x4 *>(qb + (unsigned)c * 64u + 16u * g) = qv;
+            *reinterpret_cast<u32x4 *>(qb + st_off) = qv;
             FragT gh, gl;
             {
                 const floatx4 ga = __builtin_bit_cast(floatx4, g0), gb = __builtin_bit_cast(floatx4, g1);
@@ -499,8 +501,8 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
                     gl[4 + e] = l;
                 }
             }
-            *reinterpret_cast<FragT *>(gbh + (unsigned)c * 64u + 16u * g) = gh;
-            *reinterpret_cast<FragT *>(gbl + (unsigned)c * 64u + 16u * g) = gl;
+            *reinterpret_cast<FragT *>(gbh + st_off) = gh;
+            *reinterpret_cast<FragT *>(gbl + st_off) = gl;
             const FragT qa = __builtin_bit_cast(FragT, qv);
             floatx4 s = mfma16x16x32(qa, kf, floatx4{0, 0, 0, 0});
             const floatx4 gvh = mfma16x16x32(gh, vf, floatx4{0, 0, 0, 0});
@@ -532,9 +534,10 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
             // dv^T += g^T P and dk^T += q^T dS (16x16x16: 4 queries per lane)
 #pragma unroll
             for (int dh = 0; dh < 2; ++dh) {
-                const v4i16 qt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(qb + tr_off + 32u * dh));
-                const v4i16 gth = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(gbh + tr_off + 32u * dh));
-                const v4i16 gtl = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(gbl + tr_off + 32u * dh));
+                const unsigned to = dh ? tr_off1 : tr_off0;
+                const v4i16 qt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(qb + to));
+                const v4i16 gth = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(gbh + to));
+                const v4i16 gtl = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(gbl + to));
                 dv[dh] = mfma16x16x16(gth, ph, dv[dh], T{});
                 dvl[dh] = mfma16x16x16(gth, pl, dvl[dh], T{});
                 dvl[dh] = mfma16x16x16(gtl, ph, dvl[dh], T{});

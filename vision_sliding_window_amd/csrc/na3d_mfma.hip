@@ -150,7 +150,8 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
     float m = -1e30f, l = 0.f;  // running max (shared by a query's 4 lanes) and this lane's sum
     floatx4 o[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
     unsigned char *vb0 = vbuf[wave][0], *vb1 = vbuf[wave][1];
-    const unsigned tr_off = (unsigned)(4 * g + (c >> 2)) * 64u + 8u * (unsigned)(c & 3);
+    const unsigned tr_off0 = tr_read_off(g, c, 0), tr_off1 = tr_read_off(g, c, 1);
+    const unsigned st_off = stage_off(g, c);
     const int zoff = z - (kd - 1);  // key slice minus this, times the row stride, indexes the table
 
     // logits of block (p.z, p.y, p.xb) for query c, keys 4g + r, in log2 units.
@@ -188,8 +189,8 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
         return t;
     };
     auto process = [&](const Pair &pr, const Pos &p0, const Pos &p1, int pair) {
-        *reinterpret_cast<u32x4 *>(vb0 + (unsigned)c * 64u + 16u * g) = pr.v0;
-        *reinterpret_cast<u32x4 *>(vb1 + (unsigned)c * 64u + 16u * g) = pr.v1;
+        *reinterpret_cast<u32x4 *>(vb0 + st_off) = pr.v0;
+        *reinterpret_cast<u32x4 *>(vb1 + st_off) = pr.v1;
         const floatx4 s0 = mfma16x16x32(__builtin_bit_cast(FragT, pr.k0), qf, floatx4{0, 0, 0, 0});
         const floatx4 s1 = mfma16x16x32(__builtin_bit_cast(FragT, pr.k1), qf, floatx4{0, 0, 0, 0});
         float t[8];
@@ -217,8 +218,9 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
         }
 #pragma unroll
         for (int dh = 0; dh < 2; ++dh) {
-            const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb0 + tr_off + 32u * dh));
-            const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb1 + tr_off + 32u * dh));
+            const unsigned to = dh ? tr_off1 : tr_off0;
+            const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb0 + to));
+            const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb1 + to));
             const v8i16 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             const FragT vt = __builtin_bit_cast(FragT, av);
             o[dh] = mfma16x16x32(vt, ph, o[dh] * alpha);

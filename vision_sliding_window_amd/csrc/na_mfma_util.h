@@ -60,6 +60,25 @@ __device__ inline float quad_sum(float v)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Per-wave LDS copy of a 16-position block [pos][32 dims] of 16-bit values
+// that is read back with ds_read_b64_tr_b16: the 16-byte slice s of position
+// p sits at byte p * 64 + 16 * (s ^ (p & 3)).  The XOR spreads both the
+// stores (lane (g, c) writes slice g of position c) and the transposed reads
+// (four positions per group of 16 lanes) over the banks.
+__device__ inline unsigned stage_off(int g, int c)
+{
+    return (unsigned)c * 64u + 16u * ((unsigned)g ^ ((unsigned)c & 3u));
+}
+// Where lane (g, i) reads for the transposed load of dims 16 dh .. 16 dh + 15:
+// dims 16 dh + 4 (i & 3) .. + 3 of position 4 g + (i >> 2); the lane then holds
+// dim 16 dh + i of positions 4 g .. 4 g + 3.
+__device__ inline unsigned tr_read_off(int g, int i, int dh)
+{
+    const unsigned p = 4u * g + ((unsigned)i >> 2);
+    const unsigned s = 2u * dh + ((unsigned)(i & 3) >> 1);
+    return p * 64u + 16u * (s ^ (p & 3u)) + 8u * (unsigned)(i & 1);
+}
+
 // Hide a pointer's provenance from the optimiser (an empty asm that "may
 // change" the register), so it is not re-derived from a shared base plus a
 // large per-access constant.
