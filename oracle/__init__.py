@@ -67,6 +67,8 @@ class Oracle:
         lib.na2d_oracle_window_start.restype = I
         lib.na2d_oracle_f64.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I]
         lib.na2d_oracle_f64.restype = I
+        lib.na2d_oracle_f64_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I]
+        lib.na2d_oracle_f64_lse.restype = I
         lib.na2d_oracle_f64_sampled.argtypes = [P, P, P, P, P, I64, P, I, I, I, I, I, I, I]
         lib.na2d_oracle_f64_sampled.restype = I
         self.lib = lib
@@ -91,6 +93,23 @@ class Oracle:
             raise ValueError("oracle rejected sizes B=%d heads=%d H=%d W=%d d=%d k=%d"
                              % (B, heads, H, W, d, ksize))
         return out
+
+    def na2d_forward_lse(self, q, k, v, rpb, ksize: int, nthreads: int = 0):
+        """(out, lse): the forward and each query's log softmax denominator
+        ln sum_j exp((q.k_j + B_j)/sqrt(d)), lse shaped [B, heads, H, W]."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        assert q.ndim == 5 and q.shape == k.shape == v.shape
+        B, heads, H, W, d = q.shape
+        if rpb is not None:
+            rpb = _f64(rpb)
+            assert rpb.shape == (heads, 2 * ksize - 1, 2 * ksize - 1)
+        out = np.empty_like(q)
+        lse = np.empty(q.shape[:4], dtype=np.float64)
+        rc = self.lib.na2d_oracle_f64_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(out),
+                                          _ptr(lse), B, heads, H, W, d, ksize, nthreads)
+        if rc != 0:
+            raise ValueError("oracle rejected sizes")
+        return out, lse
 
     def na2d_forward_sampled(self, q, k, v, rpb, ksize: int, idx, nthreads: int = 0):
         """Outputs [n, d] for the queries with linear index ((b*heads+h)*H+y)*W+x."""
@@ -131,6 +150,10 @@ def na2d_forward(q, k, v, rpb, ksize: int, nthreads: int = 0) -> np.ndarray:
 
 def na2d_forward_sampled(q, k, v, rpb, ksize: int, idx, nthreads: int = 0) -> np.ndarray:
     return default().na2d_forward_sampled(q, k, v, rpb, ksize, idx, nthreads)
+
+
+def na2d_forward_lse(q, k, v, rpb, ksize: int, nthreads: int = 0):
+    return default().na2d_forward_lse(q, k, v, rpb, ksize, nthreads)
 
 
 class OracleND:

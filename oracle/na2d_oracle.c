@@ -54,10 +54,13 @@ int na2d_oracle_window_start(int i, int k, int L)
     return s;
 }
 
-/* One output vector: query (b, h, y, x).  `logit` is scratch of k*k doubles. */
+/* One output vector: query (b, h, y, x).  `logit` is scratch of k*k doubles.
+ * When lse is not NULL it receives ln of the softmax denominator of Eq. 4,
+ * ln sum_j exp((Q.K_j + B_j) / sqrt(d)), the per-query statistic a backward
+ * pass can reuse. */
 static void one_query(const double *q, const double *kk, const double *v,
                       const double *rpb, int heads, int H, int W, int d, int k,
-                      int64_t b, int h, int y, int x, double *logit, double *o)
+                      int64_t b, int h, int y, int x, double *logit, double *o, double *lse)
 {
     const int64_t map = ((int64_t)b * heads + h) * H * W;   /* first pixel of this (b, h) map */
     const double *qi = q + (map + (int64_t)y * W + x) * d;
@@ -83,6 +86,7 @@ static void one_query(const double *q, const double *kk, const double *v,
     for (int j = 0; j < k * k; ++j) if (logit[j] > m) m = logit[j];
     double z = 0.0;
     for (int j = 0; j < k * k; ++j) { logit[j] = exp(logit[j] - m); z += logit[j]; }
+    if (lse) *lse = m + log(z);
     /* Eq. 4: weights times the neighbour values (Eq. 3). */
     for (int t = 0; t < d; ++t) o[t] = 0.0;
     for (int a = 0; a < k; ++a) {
@@ -101,11 +105,12 @@ static int bad_args(int B, int heads, int H, int W, int d, int k)
     return 0;
 }
 
-/* Whole forward pass.  Returns 0, or -1 on invalid sizes.  nthreads <= 0 uses
- * the OpenMP default. */
-int na2d_oracle_f64(const double *q, const double *k, const double *v,
-                    const double *rpb, double *out,
-                    int B, int heads, int H, int W, int d, int ksize, int nthreads)
+/* Whole forward pass; lse ([B, heads, H, W], may be NULL) receives each
+ * query's log softmax denominator.  Returns 0, or -1 on invalid sizes.
+ * nthreads <= 0 uses the OpenMP default. */
+int na2d_oracle_f64_lse(const double *q, const double *k, const double *v,
+                        const double *rpb, double *out, double *lse,
+                        int B, int heads, int H, int W, int d, int ksize, int nthreads)
 {
     if (bad_args(B, heads, H, W, d, ksize)) return -1;
     const int64_t rows = (int64_t)B * heads * H;
@@ -120,11 +125,20 @@ int na2d_oracle_f64(const double *q, const double *k, const double *v,
             const int64_t b = r / ((int64_t)H * heads);
             for (int x = 0; x < W; ++x)
                 one_query(q, k, v, rpb, heads, H, W, d, ksize, b, h, y, x, logit,
-                          out + (r * W + x) * d);
+                          out + (r * W + x) * d, lse ? lse + r * W + x : NULL);
         }
         free(logit);
     }
     return 0;
+}
+
+/* Whole forward pass.  Returns 0, or -1 on invalid sizes.  nthreads <= 0 uses
+ * the OpenMP default. */
+int na2d_oracle_f64(const double *q, const double *k, const double *v,
+                    const double *rpb, double *out,
+                    int B, int heads, int H, int W, int d, int ksize, int nthreads)
+{
+    return na2d_oracle_f64_lse(q, k, v, rpb, out, NULL, B, heads, H, W, d, ksize, nthreads);
 }
 
 /* The same definition for a list of queries given by their linear index
@@ -150,7 +164,7 @@ int na2d_oracle_f64_sampled(const double *q, const double *k, const double *v,
             const int y = (int)((p / W) % H);
             const int h = (int)((p / ((int64_t)W * H)) % heads);
             const int64_t b = p / ((int64_t)W * H * heads);
-            one_query(q, k, v, rpb, heads, H, W, d, ksize, b, h, y, x, logit, out + i * d);
+            one_query(q, k, v, rpb, heads, H, W, d, ksize, b, h, y, x, logit, out + i * d, NULL);
         }
         free(logit);
     }

@@ -248,5 +248,34 @@ def pin_softmax_shift(orc):
     assert np.abs(a - b).max() <= 1e-10, np.abs(a - b).max()
 
 
+def pin_lse(orc):
+    """The log softmax denominator ln sum_j exp(s_j), s_j = (q.k_j + B_j)/sqrt(d):
+    with Q = 0 and no bias every logit is 0, so it is ln(k^2) exactly; at
+    k = H = W it is scipy's logsumexp of the dense logits of full self
+    attention; a constant c added to the bias adds c/sqrt(d); and the output
+    returned beside it is the pinned forward's, bit for bit."""
+    from scipy.special import logsumexp
+    r = _rng(19)
+    v = r.standard_normal((2, 2, 9, 11, 8))
+    for ks in (1, 3, 5, 9):
+        _, lse = orc.na2d_forward_lse(np.zeros_like(v), v, v, None, ks)
+        assert np.abs(lse - np.log(ks * ks)).max() <= 1e-12, ("box", ks)
+    for (B, heads, n, d) in [(1, 2, 5, 8), (2, 1, 7, 32)]:
+        q = r.standard_normal((B, heads, n, n, d)) * 2.0
+        k = r.standard_normal((B, heads, n, n, d))
+        vv = r.standard_normal((B, heads, n, n, d))
+        rpb = r.standard_normal((heads, 2 * n - 1, 2 * n - 1))
+        out, lse = orc.na2d_forward_lse(q, k, vv, rpb, n)
+        for b in range(B):
+            for h in range(heads):
+                S = q[b, h].reshape(n * n, d) @ k[b, h].reshape(n * n, d).T
+                S = (S + _dense_bias(rpb[h], n, n, n)) / np.sqrt(d)
+                want = logsumexp(S, axis=1).reshape(n, n)
+                assert np.abs(lse[b, h] - want).max() <= 1e-12, ("dense", n)
+        _, shifted = orc.na2d_forward_lse(q, k, vv, rpb + 3.0, n)
+        assert np.abs(shifted - lse - 3.0 / np.sqrt(d)).max() <= 1e-12, ("shift", n)
+        assert np.array_equal(out, orc.na2d_forward(q, k, vv, rpb, n))
+
+
 ALL_PINS = [pin_span, pin_self_attention, pin_sdpa, pin_translation, pin_flip_transpose,
-            pin_box_mean, pin_identity, pin_bias_offset, pin_softmax_shift]
+            pin_box_mean, pin_identity, pin_bias_offset, pin_softmax_shift, pin_lse]

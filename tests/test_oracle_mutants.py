@@ -26,6 +26,8 @@ MUTANTS = {
                        "const double w = logit[a * k + c] / (z + 1e-3);"),
     "key_query_mixup": ("const double *kj = kk + (map + (int64_t)ky * W + kx) * d;",
                         "const double *kj = q + (map + (int64_t)ky * W + kx) * d;"),
+    "lse_without_max": ("if (lse) *lse = m + log(z);", "if (lse) *lse = log(z);"),
+    "lse_log2": ("if (lse) *lse = m + log(z);", "if (lse) *lse = m + log2(z);"),
 }
 
 
