@@ -127,11 +127,13 @@ def cpu_baseline(w, x, seconds: float = 10.0):
                       % (n, w.name, done // n, el)}
 
 
-def backward_bytes(w) -> int:
-    """Bytes the gradients must move: read q, k, v, out and dout, write dq, dk,
-    dv once, read the bias table and write its gradient."""
+def backward_bytes(w, with_lse: bool = False) -> int:
+    """Bytes the gradients must move: read q, k, v, out and dout (and the
+    forward's per-query log-sum-exp when it is reused), write dq, dk, dv once,
+    read the bias table and write its gradient."""
     es = 4 if w.dtype == "f32" else 2
-    return w.queries * (3 * w.d * es + 2 * 4 * w.d + 3 * 4 * w.d) + 2 * 4 * math.prod(w.rpb_shape)
+    per_query = 3 * w.d * es + 2 * 4 * w.d + 3 * 4 * w.d + (4 if with_lse else 0)
+    return w.queries * per_query + 2 * 4 * math.prod(w.rpb_shape)
 
 
 def bench_backward(args, w, wname, lib, dev, dtype_code):
@@ -139,27 +141,33 @@ def bench_backward(args, w, wname, lib, dev, dtype_code):
     from vision_sliding_window_amd import na2d
     from vision_sliding_window_amd.inputs import workload_inputs
     x = workload_inputs(w, seed=0)
-    set_bytes = backward_bytes(w)
+    set_bytes = backward_bytes(w, with_lse=not args.recompute_stats)
     nsets = max(1, math.ceil(args.min_footprint_gib * 2 ** 30 / set_bytes))
     rpb = x.rpb.to(dev)
     q0, k0, v0 = x.q.to(dev), x.k.to(dev), x.v.to(dev)
-    out0 = na2d.forward(q0, k0, v0, rpb, w.k)
+    # the training forward: out and each query's log-sum-exp, which the
+    # backward reuses unless --recompute-stats asks it to recompute them
+    out0, lse0 = na2d.forward_lse(q0, k0, v0, rpb, w.k)
+    if args.recompute_stats:
+        lse0 = None
     g0 = torch.randn(w.shape, generator=torch.Generator().manual_seed(1)).to(dev)
     ws_bytes = na2d.na2d_backward_workspace_bytes(w.B, w.heads, w.H, w.W, w.k)
     f32 = dict(dtype=torch.float32, device=dev)
     sets = []
     for i in range(nsets):
         c = (lambda t: t.clone()) if i else (lambda t: t)
-        sets.append((c(q0), c(k0), c(v0), c(out0), c(g0), torch.empty(w.shape, **f32),
+        sets.append((c(q0), c(k0), c(v0), c(out0), None if lse0 is None else c(lse0), c(g0),
+                     torch.empty(w.shape, **f32),
                      torch.empty(w.shape, **f32), torch.empty(w.shape, **f32),
                      torch.empty(rpb.shape, **f32), torch.empty(ws_bytes // 4, **f32)))
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
     def launch(i):
-        q, k, v, out, g, dq, dk, dv, drpb, ws = sets[i % nsets]
+        q, k, v, out, lse, g, dq, dk, dv, drpb, ws = sets[i % nsets]
         st = lib.na2d_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
-                               out.data_ptr(), g.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               out.data_ptr(), None if lse is None else lse.data_ptr(),
+                               g.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                dv.data_ptr(), drpb.data_ptr(), ws.data_ptr(), w.B, w.heads, w.H,
                                w.W, w.d, w.k, dtype_code, sptr)
         if st != 0:
@@ -187,6 +195,7 @@ def bench_backward(args, w, wname, lib, dev, dtype_code):
                    # 16-bit inputs with d = 32 and k <= 25 run on the matrix cores
                    "kernel": "mfma" if w.dtype != "f32" and w.d == 32 and w.k <= 25 else "valu",
                    "roofline_scope": "whole backward (all its kernels)",
+                   "softmax_stats": "recomputed" if lse0 is None else "from the forward (lse)",
                    "algorithmic_bytes_per_step": set_bytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -235,6 +244,8 @@ def main():
     ap.add_argument("--hot", action="store_true",
                     help="also time one cache-resident input set (reported separately)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--recompute-stats", action="store_true",
+                    help="--backward without the forward's log-sum-exp (the backward recomputes it)")
     ap.add_argument("--backward", action="store_true",
                     help="time the NA2D gradients (na2d_backward) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

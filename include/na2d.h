@@ -102,6 +102,14 @@ enum {
 int na2d_forward(const void *q, const void *k, const void *v, const float *rpb, float *out,
                  int B, int heads, int H, int W, int d, int ksize, int dtype, void *stream);
 
+/* na2d_forward that also writes, per query, the natural log of the softmax
+ * denominator: lse = ln sum_j exp((q.k_j + B_j) / sqrt(d)) over the window
+ * ([B, heads, H, W] float32, 16-byte aligned, overlapping nothing else;
+ * NULL is NA2D_ERR_NULL).  The training forward: na2d_backward reuses it. */
+int na2d_forward_lse(const void *q, const void *k, const void *v, const float *rpb, float *out,
+                     float *lse, int B, int heads, int H, int W, int d, int ksize, int dtype,
+                     void *stream);
+
 /* The same operation with the kernel family forced by `algo` (na2d_algo).
  * NA2D_ERR_UNSUPPORTED if that family cannot run these sizes or dtype. */
 int na2d_forward_ex(const void *q, const void *k, const void *v, const float *rpb, float *out,
@@ -185,7 +193,10 @@ int sasa2d_forward(const void *q, const void *k, const void *v, const float *rpb
  * ([B, heads, H, W, d] float32, overwritten) and, when rpb is not NULL,
  * drpb = dL/drpb ([heads, 2k-1, 2k-1] float32, overwritten; it must be NULL
  * when rpb is).  q, k, v, rpb, ksize and dtype are those of the forward call;
- * out is its float32 output and dout is float32 [B, heads, H, W, d].
+ * out is its float32 output and dout is float32 [B, heads, H, W, d].  lse is
+ * the per-query log-sum-exp that na2d_forward_lse wrote in the same forward
+ * call ([B, heads, H, W] float32), or NULL: with it the backward reuses the
+ * forward's softmax statistics instead of recomputing them.
  *
  * `workspace` is caller-owned device memory of na2d_backward_workspace_bytes
  * bytes (16-byte aligned, contents ignored on entry): the first kernel leaves
@@ -199,8 +210,8 @@ int sasa2d_forward(const void *q, const void *k, const void *v, const float *rpb
  * for na2d_forward.
  * ------------------------------------------------------------------------ */
 int na2d_backward(const void *q, const void *k, const void *v, const float *rpb,
-                  const float *out, const float *dout, float *dq, float *dk, float *dv,
-                  float *drpb, void *workspace, int B, int heads, int H, int W, int d,
+                  const float *out, const float *lse, const float *dout, float *dq, float *dk,
+                  float *dv, float *drpb, void *workspace, int B, int heads, int H, int W, int d,
                   int ksize, int dtype, void *stream);
 
 /* Bytes of workspace na2d_backward needs for these sizes and window (0 if
@@ -209,10 +220,10 @@ long long na2d_backward_workspace_bytes(int B, int heads, int H, int W, int ksiz
 
 /* Host-only check of na2d_backward's arguments (no HIP call). */
 int na2d_backward_check_args(const void *q, const void *k, const void *v, const float *rpb,
-                             const float *out, const float *dout, const float *dq,
-                             const float *dk, const float *dv, const float *drpb,
-                             const void *workspace, int B, int heads, int H, int W, int d,
-                             int ksize, int dtype);
+                             const float *out, const float *lse, const float *dout,
+                             const float *dq, const float *dk, const float *dv,
+                             const float *drpb, const void *workspace, int B, int heads, int H,
+                             int W, int d, int ksize, int dtype);
 
 /* Static text for a status code. */
 const char *na2d_strerror(int status);

@@ -121,6 +121,16 @@ def test_forward_rejects_before_launch():
     """Invalid calls return their status without touching the GPU."""
     st = na2d.na2d_forward(Q, K, V, RPB, OUT, 2, 2, 14, 15, 32, 8, na2d.NA2D_F16, None)
     assert st == na2d.NA2D_ERR_KSIZE
+    lse = 0xC0000000
+    st = na2d.na2d_forward_lse(Q, K, V, RPB, OUT, None, 2, 2, 14, 15, 32, 7, na2d.NA2D_F16, None)
+    assert st == na2d.NA2D_ERR_NULL
+    st = na2d.na2d_forward_lse(Q, K, V, RPB, OUT, lse + 4, 2, 2, 14, 15, 32, 7, na2d.NA2D_F16, None)
+    assert st == na2d.NA2D_ERR_ALIGN
+    st = na2d.na2d_forward_lse(Q, K, V, RPB, OUT, OUT + 64, 2, 2, 14, 15, 32, 7, na2d.NA2D_F16,
+                               None)
+    assert st == na2d.NA2D_ERR_ALIAS
+    st = na2d.na2d_forward_lse(Q, K, V, RPB, OUT, lse, 2, 2, 14, 15, 32, 8, na2d.NA2D_F16, None)
+    assert st == na2d.NA2D_ERR_KSIZE
     st = na2d.na2d_forward_ex(Q, K, V, RPB, Q, 2, 2, 14, 15, 32, 7, na2d.NA2D_F16, 0, None)
     assert st == na2d.NA2D_ERR_ALIAS
 
@@ -212,14 +222,16 @@ def test_nd_wrappers_reject_before_launch():
 
 
 DQ, DK, DV, DRPB, WS, DOUT = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000, 0xB0000000
+LSE = 0xC0000000
 
 
 def check_bwd(B=2, heads=2, H=14, W=15, d=32, ksize=7, dtype=na2d.NA2D_F16, **ptr):
-    p = dict(q=Q, k=K, v=V, rpb=RPB, out=OUT, dout=DOUT, dq=DQ, dk=DK, dv=DV, drpb=DRPB, ws=WS)
+    p = dict(q=Q, k=K, v=V, rpb=RPB, out=OUT, lse=None, dout=DOUT, dq=DQ, dk=DK, dv=DV,
+             drpb=DRPB, ws=WS)
     p.update(ptr)
-    return na2d.na2d_backward_check_args(p["q"], p["k"], p["v"], p["rpb"], p["out"], p["dout"],
-                                         p["dq"], p["dk"], p["dv"], p["drpb"], p["ws"], B, heads,
-                                         H, W, d, ksize, dtype)
+    return na2d.na2d_backward_check_args(p["q"], p["k"], p["v"], p["rpb"], p["out"], p["lse"],
+                                         p["dout"], p["dq"], p["dk"], p["dv"], p["drpb"], p["ws"],
+                                         B, heads, H, W, d, ksize, dtype)
 
 
 def test_backward_args():
@@ -236,13 +248,18 @@ def test_backward_args():
     assert check_bwd(dk=DQ + 64) == na2d.NA2D_ERR_ALIAS       # two outputs overlap
     assert check_bwd(ws=DOUT + 16) == na2d.NA2D_ERR_ALIAS
     assert check_bwd(ws=DOUT - 4096) == na2d.NA2D_ERR_ALIAS   # the bias-gradient tables reach dout
+    # the forward's log-sum-exp: optional, aligned, written by nothing here
+    assert check_bwd(lse=LSE) == na2d.NA2D_OK
+    assert check_bwd(lse=LSE + 4) == na2d.NA2D_ERR_ALIGN
+    assert check_bwd(lse=LSE, dq=LSE - 16) == na2d.NA2D_ERR_ALIAS
+    assert check_bwd(lse=LSE, ws=LSE + 2 * 2 * 14 * 15 * 4 - 16) == na2d.NA2D_ERR_ALIAS
     # statistics (8 bytes a query, padded to 256) then a (2k-1)^2 table per 8 x 8 tile
     stats = (2 * 2 * 14 * 15 * 8 + 255) // 256 * 256
     assert na2d.na2d_backward_workspace_bytes(2, 2, 14, 15, 5) == stats + 2 * 2 * 2 * 2 * 81 * 4
     assert na2d.na2d_backward_workspace_bytes(0, 2, 14, 15, 5) == 0
     assert na2d.na2d_backward_workspace_bytes(2, 2, 14, 15, 0) == 0
-    st = na2d.na2d_backward(Q, K, V, RPB, OUT, DOUT, DQ, DK, DV, DRPB, WS, 2, 2, 14, 15, 32, 17,
-                            na2d.NA2D_F16, None)
+    st = na2d.na2d_backward(Q, K, V, RPB, OUT, None, DOUT, DQ, DK, DV, DRPB, WS, 2, 2, 14, 15, 32,
+                            17, na2d.NA2D_F16, None)
     assert st == na2d.NA2D_ERR_KSIZE                          # rejected before any launch
 
 

@@ -249,7 +249,7 @@ hipError_t launch_typed(const Problem &p, hipStream_t stream)
 hipError_t launch_mfma_1d(const Problem &p, hipStream_t stream)
 {
     if (p.d != 32 || p.depth != 1 || p.H != 1 || p.kd != 1 || p.kh != 1 || p.mode != NA_WINDOW_NA ||
-        p.kw < 3 || p.kw > NA1D_MFMA_MAX_KSIZE || (uint64_t)p.W * 128u > 0x7fffffffull)
+        p.kw < 3 || p.kw > NA1D_MFMA_MAX_KSIZE || (uint64_t)p.W * 128u > 0x7fffffffull || p.lse)
         return hipErrorInvalidValue;
     if (p.dtype == NA2D_F16) return launch_typed<_Float16>(p, stream);
     if (p.dtype == NA2D_BF16) return launch_typed<__bf16>(p, stream);

@@ -94,7 +94,7 @@ int resolve_algo(const Nd &n, int dtype, int algo)
 }
 
 int check_nd(const void *q, const void *k, const void *v, const float *rpb, const float *out,
-             const Nd &n, int dtype, int algo)
+             const Nd &n, int dtype, int algo, const float *lse = nullptr)
 {
     if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
     if (algo != NA2D_ALGO_AUTO && algo != NA2D_ALGO_VALU && algo != NA2D_ALGO_MFMA)
@@ -103,16 +103,24 @@ int check_nd(const void *q, const void *k, const void *v, const float *rpb, cons
     if (!q || !k || !v || !out) return NA2D_ERR_NULL;
     const int st = check_sizes(n);
     if (st != NA2D_OK) return st;
-    const void *ptrs[5] = {q, k, v, out, rpb};
+    const void *ptrs[6] = {q, k, v, out, rpb, lse};
     for (const void *p : ptrs)
         if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return NA2D_ERR_ALIGN;
-    const uint64_t elems = (uint64_t)n.B * n.heads * n.D * n.H * n.W * n.d;
+    const uint64_t queries = (uint64_t)n.B * n.heads * n.D * n.H * n.W;
+    const uint64_t elems = queries * n.d;
     const uint64_t in_bytes = elems * elem_size(dtype), out_bytes = elems * 4;
     const uint64_t rpb_bytes =
         (uint64_t)n.heads * (2 * n.kd - 1) * (2 * n.kh - 1) * (2 * n.kw - 1) * 4;
     if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
         overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, rpb, rpb_bytes))
         return NA2D_ERR_ALIAS;
+    if (lse) {  // the log-sum-exp output: overlaps nothing
+        const uint64_t lse_bytes = queries * 4;
+        if (overlaps(lse, lse_bytes, q, in_bytes) || overlaps(lse, lse_bytes, k, in_bytes) ||
+            overlaps(lse, lse_bytes, v, in_bytes) || overlaps(lse, lse_bytes, rpb, rpb_bytes) ||
+            overlaps(lse, lse_bytes, out, out_bytes))
+            return NA2D_ERR_ALIAS;
+    }
     const int a = resolve_algo(n, dtype, algo);
     if (a == NA2D_ALGO_VALU && !valu_supports(n)) return NA2D_ERR_UNSUPPORTED;
     if (a == NA2D_ALGO_MFMA && !mfma_supports(n, dtype)) return NA2D_ERR_UNSUPPORTED;
@@ -120,13 +128,13 @@ int check_nd(const void *q, const void *k, const void *v, const float *rpb, cons
 }
 
 int forward_nd(const void *q, const void *k, const void *v, const float *rpb, float *out,
-               const Nd &n, int dtype, int algo, void *stream)
+               const Nd &n, int dtype, int algo, void *stream, float *lse = nullptr)
 {
-    const int st = check_nd(q, k, v, rpb, out, n, dtype, algo);
+    const int st = check_nd(q, k, v, rpb, out, n, dtype, algo, lse);
     if (st != NA2D_OK) return st;
     const na2d::Problem p{q,     k,      v,   rpb,  out,  n.B,  n.heads, n.H,
                           n.W,   n.d,    n.kh, dtype, n.D, n.kd, n.kh,    n.kw,
-                          n.mode};
+                          n.mode, lse};
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (resolve_algo(n, dtype, algo) == NA2D_ALGO_MFMA)
@@ -197,6 +205,15 @@ extern "C" int na2d_forward(const void *q, const void *k, const void *v, const f
                            stream);
 }
 
+extern "C" int na2d_forward_lse(const void *q, const void *k, const void *v, const float *rpb,
+                                float *out, float *lse, int B, int heads, int H, int W, int d,
+                                int ksize, int dtype, void *stream)
+{
+    if (!lse) return NA2D_ERR_NULL;
+    return forward_nd(q, k, v, rpb, out, nd_2d(B, heads, H, W, d, ksize, NA_WINDOW_NA), dtype,
+                      NA2D_ALGO_AUTO, stream, lse);
+}
+
 extern "C" int na_check_args_nd(const void *q, const void *k, const void *v, const float *rpb,
                                 const float *out, int B, int heads, int D, int H, int W, int d,
                                 int kd, int kh, int kw, int mode, int dtype, int algo)
@@ -240,9 +257,9 @@ extern "C" int sasa2d_forward(const void *q, const void *k, const void *v, const
 namespace {
 
 int check_backward(const void *q, const void *k, const void *v, const float *rpb,
-                   const float *out, const float *dout, const float *dq, const float *dk,
-                   const float *dv, const float *drpb, const void *ws, int B, int heads, int H,
-                   int W, int d, int ksize, int dtype)
+                   const float *out, const float *lse, const float *dout, const float *dq,
+                   const float *dk, const float *dv, const float *drpb, const void *ws, int B,
+                   int heads, int H, int W, int d, int ksize, int dtype)
 {
     if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
     if (!q || !k || !v || !out || !dout || !dq || !dk || !dv || !ws) return NA2D_ERR_NULL;
@@ -250,7 +267,7 @@ int check_backward(const void *q, const void *k, const void *v, const float *rpb
     const Nd n = nd_2d(B, heads, H, W, d, ksize, NA_WINDOW_NA);
     const int st = check_sizes(n);
     if (st != NA2D_OK) return st;
-    const void *ptrs[11] = {q, k, v, rpb, out, dout, dq, dk, dv, drpb, ws};
+    const void *ptrs[12] = {q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, ws};
     for (const void *p : ptrs)
         if (p && (reinterpret_cast<uintptr_t>(p) & 15u)) return NA2D_ERR_ALIGN;
     const uint64_t queries = (uint64_t)B * heads * H * W, elems = queries * d;
@@ -259,7 +276,8 @@ int check_backward(const void *q, const void *k, const void *v, const float *rpb
     const uint64_t rpb_b = (uint64_t)heads * (2 * ksize - 1) * (2 * ksize - 1) * 4;
     struct Span { const void *p; uint64_t n; };
     const Span outs[5] = {{dq, f_b}, {dk, f_b}, {dv, f_b}, {drpb, rpb_b}, {ws, ws_b}};
-    const Span ins[6] = {{q, in_b}, {k, in_b}, {v, in_b}, {rpb, rpb_b}, {out, f_b}, {dout, f_b}};
+    const Span ins[7] = {{q, in_b}, {k, in_b}, {v, in_b}, {rpb, rpb_b}, {out, f_b}, {dout, f_b},
+                         {lse, queries * 4}};
     for (int i = 0; i < 5; ++i) {
         for (const Span &in : ins)
             if (overlaps(outs[i].p, outs[i].n, in.p, in.n)) return NA2D_ERR_ALIAS;
@@ -273,13 +291,14 @@ int check_backward(const void *q, const void *k, const void *v, const float *rpb
 }  // namespace
 
 extern "C" int na2d_backward_check_args(const void *q, const void *k, const void *v,
-                                        const float *rpb, const float *out, const float *dout,
-                                        const float *dq, const float *dk, const float *dv,
-                                        const float *drpb, const void *workspace, int B,
-                                        int heads, int H, int W, int d, int ksize, int dtype)
+                                        const float *rpb, const float *out, const float *lse,
+                                        const float *dout, const float *dq, const float *dk,
+                                        const float *dv, const float *drpb,
+                                        const void *workspace, int B, int heads, int H, int W,
+                                        int d, int ksize, int dtype)
 {
-    return check_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads, H, W,
-                          d, ksize, dtype);
+    return check_backward(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, workspace, B, heads, H,
+                          W, d, ksize, dtype);
 }
 
 extern "C" long long na2d_backward_workspace_bytes(int B, int heads, int H, int W, int ksize)
@@ -290,15 +309,15 @@ extern "C" long long na2d_backward_workspace_bytes(int B, int heads, int H, int 
 }
 
 extern "C" int na2d_backward(const void *q, const void *k, const void *v, const float *rpb,
-                             const float *out, const float *dout, float *dq, float *dk,
-                             float *dv, float *drpb, void *workspace, int B, int heads, int H,
-                             int W, int d, int ksize, int dtype, void *stream)
+                             const float *out, const float *lse, const float *dout, float *dq,
+                             float *dk, float *dv, float *drpb, void *workspace, int B,
+                             int heads, int H, int W, int d, int ksize, int dtype, void *stream)
 {
-    const int st = check_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads,
-                                  H, W, d, ksize, dtype);
+    const int st = check_backward(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, workspace, B,
+                                  heads, H, W, d, ksize, dtype);
     if (st != NA2D_OK) return st;
-    const na2d::BwdProblem p{q,  k,  v,    rpb,       out, dout,  dq, dk, dv,
-                             drpb, workspace, B, heads, H, W, d, ksize, dtype};
+    const na2d::BwdProblem p{q,  k,    v,         rpb, out, lse,   dout, dq, dk,
+                             dv, drpb, workspace, B,   heads, H, W, d, ksize, dtype};
     const hipError_t e = na2d::launch_backward(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         g_last_error = hipGetErrorString(e);

@@ -73,6 +73,7 @@ __device__ inline void load_row(const T *__restrict__ p, float (&dst)[D])
 struct BwdArgs {
     const void *q, *k, *v;
     const float *rpb, *out, *dout;
+    const float *lse_in;  // the forward's per-query log-sum-exp (natural log), or null
     float *dq, *dk, *dv, *drpb;
     float2 *ws;  // per query: (log2-sum-exp of the log2-scaled logits, g . o)
     int heads, H, W, ks;
@@ -123,26 +124,33 @@ __global__ __launch_bounds__(kThreadsB) void bwd_query_kernel(BwdArgs a)
         const float *bias = a.rpb ? a.rpb + (int64_t)h * nb * nb : nullptr;
         const T *kk = static_cast<const T *>(a.k);
         const T *vv = static_cast<const T *>(a.v);
-        // pass 1: softmax statistics (online max and sum, log2 units)
-        float m = -INFINITY, l = 0.f;
-        for (int ay = 0; ay < ks; ++ay) {
-            const int64_t row = base + (int64_t)(sy + ay) * W;
-            for (int ax = 0; ax < ks; ++ax) {
-                float kf[D];
-                load_row<T, D>(kk + (row + sx + ax) * D, kf);
-                float dot = 0.f;
+        // pass 1: softmax statistics (online max and sum, log2 units), unless
+        // the forward's log-sum-exp is given
+        float lse;
+        if (a.lse_in) {
+            lse = a.lse_in[qi] * 1.4426950408889634f;  // to log2 units
+        } else {
+            float m = -INFINITY, l = 0.f;
+            for (int ay = 0; ay < ks; ++ay) {
+                const int64_t row = base + (int64_t)(sy + ay) * W;
+                for (int ax = 0; ax < ks; ++ax) {
+                    float kf[D];
+                    load_row<T, D>(kk + (row + sx + ax) * D, kf);
+                    float dot = 0.f;
 #pragma unroll
-                for (int e = 0; e < D; ++e) dot = fmaf(qf[e], kf[e], dot);
-                const float b = bias ? bias[(sy + ay - y + ks - 1) * nb + (sx + ax - x + ks - 1)] : 0.f;
-                const float s = (dot + b) * a.c;
-                if (s > m) {
-                    l *= exp2f(m - s);
-                    m = s;
+                    for (int e = 0; e < D; ++e) dot = fmaf(qf[e], kf[e], dot);
+                    const float b =
+                        bias ? bias[(sy + ay - y + ks - 1) * nb + (sx + ax - x + ks - 1)] : 0.f;
+                    const float s = (dot + b) * a.c;
+                    if (s > m) {
+                        l *= exp2f(m - s);
+                        m = s;
+                    }
+                    l += exp2f(s - m);
                 }
-                l += exp2f(s - m);
             }
+            lse = m + log2f(l);
         }
-        const float lse = m + log2f(l);
         a.ws[qi] = make_float2(lse, go);
         // pass 2: dS_ij, dq_i and the bias gradient
         float dqf[D];
@@ -253,6 +261,7 @@ hipError_t launch_bwd_typed(const BwdProblem &p, hipStream_t stream)
     a.v = p.v;
     a.rpb = p.rpb;
     a.out = p.out;
+    a.lse_in = p.lse;
     a.dout = p.dout;
     a.dq = p.dq;
     a.dk = p.dk;

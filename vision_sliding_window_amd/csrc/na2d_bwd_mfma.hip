@@ -105,6 +105,7 @@ __device__ inline void holders(int j, int ks, int L, int &lo, int &hi)
 struct BArgs {
     const void *q, *k, *v;
     const float *rpb, *out, *dout;
+    const float *lse_in;  // the forward's per-query log-sum-exp (natural log), or null
     float *dq, *dk, *dv, *drpb;
     float2 *ws;
     float *part;  // per-tile bias-gradient tables, (2k-1)^2 floats each
@@ -294,35 +295,42 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
         const int nblk = (kxhi - kxlo + 16) >> 4;
         const int nblocks = (kyhi - kylo + 1) * nblk;
 
-        // pass 1: online max and sum of the log2-scaled logits, per lane over
-        // its keys 4g..4g+3 of each block, then over the four lane groups.
-        // Blocks run row by row.
-        float m = -1e30f, l = 0.f;
-        pipelined_walk(
-            BlockWalk(kylo, kyhi, kxlo, nblk), nblocks,
-            [&](int ky, int kxb) { return load_slice(rk, ky, kxb + c, W, g); },
-            [&](const u32x4 &kv, int ky, int kxb) {
-                const FragT ka = __builtin_bit_cast(FragT, kv);
-                const bool rowin = own_valid && (unsigned)(ky - sy) < (unsigned)ks;
-                const int brow = (ky - qy + ks - 1) * nb;
-                const floatx4 s = mfma16x16x32(ka, qf, floatx4{0, 0, 0, 0});
-                float t[4];
+        // the softmax statistics: the forward's log-sum-exp when given, else
+        // pass 1 below recomputes them
+        float lse = 0.f;
+        if (a.lse_in) {
+            if (own_valid) lse = a.lse_in[qi] * 1.4426950408889634f;  // to log2 units
+        } else {
+            // pass 1: online max and sum of the log2-scaled logits, per lane over
+            // its keys 4g..4g+3 of each block, then over the four lane groups.
+            // Blocks run row by row.
+            float m = -1e30f, l = 0.f;
+            pipelined_walk(
+                BlockWalk(kylo, kyhi, kxlo, nblk), nblocks,
+                [&](int ky, int kxb) { return load_slice(rk, ky, kxb + c, W, g); },
+                [&](const u32x4 &kv, int ky, int kxb) {
+                    const FragT ka = __builtin_bit_cast(FragT, kv);
+                    const bool rowin = own_valid && (unsigned)(ky - sy) < (unsigned)ks;
+                    const int brow = (ky - qy + ks - 1) * nb;
+                    const floatx4 s = mfma16x16x32(ka, qf, floatx4{0, 0, 0, 0});
+                    float t[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int kx = kxb + 4 * g + r;
-                    const bool in = rowin && (unsigned)(kx - sx) < (unsigned)ks;
-                    const float b = table_at(raw, brow + kx - qx + ks - 1, nb * nb);
-                    t[r] = in ? s[r] * a.c + b : -INFINITY;
-                }
-                const float mn = fmaxf(fmaxf(m, fmaxf(t[0], t[1])), fmaxf(t[2], t[3]));
-                l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(t[0] - mn) +
-                    __builtin_amdgcn_exp2f(t[1] - mn) + __builtin_amdgcn_exp2f(t[2] - mn) +
-                    __builtin_amdgcn_exp2f(t[3] - mn);
-                m = mn;
-            });
-        const float mq = quad_max(m);
-        const float lq = quad_sum(l * __builtin_amdgcn_exp2f(m - mq));
-        const float lse = own_valid ? mq + __builtin_amdgcn_logf(lq) : 0.f;
+                    for (int r = 0; r < 4; ++r) {
+                        const int kx = kxb + 4 * g + r;
+                        const bool in = rowin && (unsigned)(kx - sx) < (unsigned)ks;
+                        const float b = table_at(raw, brow + kx - qx + ks - 1, nb * nb);
+                        t[r] = in ? s[r] * a.c + b : -INFINITY;
+                    }
+                    const float mn = fmaxf(fmaxf(m, fmaxf(t[0], t[1])), fmaxf(t[2], t[3]));
+                    l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(t[0] - mn) +
+                        __builtin_amdgcn_exp2f(t[1] - mn) + __builtin_amdgcn_exp2f(t[2] - mn) +
+                        __builtin_amdgcn_exp2f(t[3] - mn);
+                    m = mn;
+                });
+            const float mq = quad_max(m);
+            const float lq = quad_sum(l * __builtin_amdgcn_exp2f(m - mq));
+            lse = own_valid ? mq + __builtin_amdgcn_logf(lq) : 0.f;
+        }
 
         // pass 2: P, dS, dq^T += k^T dS^T and the bias gradient
         floatx4 dq[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
@@ -574,6 +582,7 @@ hipError_t launch_backward_mfma(const BwdProblem &p, hipStream_t stream)
     a.v = p.v;
     a.rpb = p.rpb;
     a.out = p.out;
+    a.lse_in = p.lse;
     a.dout = p.dout;
     a.dq = p.dq;
     a.dk = p.dk;

@@ -15,12 +15,13 @@ struct Problem {
     float *out;
     int B, heads, H, W, d, ksize, dtype;
     int depth, kd, kh, kw, mode;
+    float *lse = nullptr;  // per-query log-sum-exp of the logits (NA 2D only), or null
 };
 
 // One validated backward problem (include/na2d.h, na2d_backward).
 struct BwdProblem {
     const void *q, *k, *v;
-    const float *rpb, *out, *dout;
+    const float *rpb, *out, *lse, *dout;  // lse: the forward's, or null (recomputed)
     float *dq, *dk, *dv, *drpb;
     void *workspace;
     int B, heads, H, W, d, ksize, dtype;

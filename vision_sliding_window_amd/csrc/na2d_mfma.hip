@@ -74,6 +74,7 @@ struct Args {
     const void *q, *k, *v;
     const float *rpb;
     float *out;
+    float *lse;            // per-query log-sum-exp of the logits, or null
     int B, heads, H, W, ks;
     int tiles_x, tiles_y;  // tiles per map
     unsigned ntiles;       // heads * B * tiles_y * tiles_x
@@ -313,10 +314,18 @@ __device__ inline void stage_tile(const Args &a, const Tile &t, unsigned char *s
 //  kGeneral:  split layout, general table with per-row / per-column indices.
 enum { kClass = 0, kInterior = 1, kGeneral = 2 };
 
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int MODE, int WM, bool CT>
+// With LSE, also leaves the running max (log2 units, shared by a query's four
+// lanes) in st.m and, in st.l, this lane's softmax sum over the unrounded
+// weights (the fp16 path's lsum sums the weights as rounded to fp16).
+struct SoftStats {
+    float m, l;
+};
+
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int MODE, int WM, bool CT, bool LSE = false>
 __device__ inline void attend(const Args &a, const Tile &t, const unsigned char *smem,
                               const float *btab, int lr, int wave, int ry, int lane,
-                              const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum)
+                              const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum,
+                              SoftStats &st)
 {
     using S = Shape<QY, QX, NCB, RPC, kWaves, CT>;
     using FragT = typename Frag<T>::type;
@@ -377,6 +386,7 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 
     float m = -__builtin_inff();
     lsum = 0.f;
+    float lex = 0.f;
     o[0] = floatx4{0.f, 0.f, 0.f, 0.f};
     o[1] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -424,6 +434,7 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
         if (c0 > 0) {  // rescale what earlier chunks accumulated
             const float corr = __builtin_amdgcn_exp2f(m - muse);
             lsum *= corr;
+            if constexpr (LSE) lex *= corr;
 #pragma unroll
             for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
@@ -459,6 +470,10 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 #pragma unroll
                 for (int j = 0; j < 8; j += 2)
                     lsum = __builtin_amdgcn_fdot2(half2{pf[j], pf[j + 1]}, half2{1, 1}, lsum, false);
+                if constexpr (LSE) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) lex += p[j];
+                }
 #pragma unroll
                 for (int dh = 0; dh < 2; ++dh) o[dh] = mfma16x16x32(vf[dh], pf, o[dh]);
             } else {
@@ -485,14 +500,19 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
             bp += RPC * P;
         }
     }
+    if constexpr (LSE) {
+        st.m = m;
+        st.l = __is_same(T, _Float16) ? lex : lsum;
+    }
 }
 
 // One wave's share of a tile: choose its candidate key rows and the bias
 // path, leave o / lsum for store_out.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT = true>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT = true, bool LSE = false>
 __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned char *smem,
                                    const float *btab, int lr, int wave, int lane,
-                                   const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum)
+                                   const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum,
+                                   SoftStats &st)
 {
     using S = Shape<QY, QX, NCB, RPC, kWaves, CT>;
     const int ks = KS ? KS : a.ks, H = a.H, W = a.W, r = ks >> 1;
@@ -500,8 +520,8 @@ __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned 
     const int y1 = t.y0 + QY * wave;
     const int ry = max(t.hy0, min(window_start<WM>(min(y1, H - 1), ks, H), t.hy0 + t.hr - nr));
     if constexpr (S::CLS) {
-        attend<T, QY, QX, NCB, RPC, KS, kClass, WM, CT>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
-                                                    lsum);
+        attend<T, QY, QX, NCB, RPC, KS, kClass, WM, CT, LSE>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
+                                                         lsum, st);
     } else {
         // no query window clamped (SASA windows never are), and the candidate
         // rows / columns start k/2 above / left of the subtile's first query
@@ -510,24 +530,31 @@ __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned 
                                 t.x0 + QX - 1 + r <= W - 1);
         const bool interior = unclamped && ry == y1 - r && t.cx == t.x0 - r;
         if (interior)
-            attend<T, QY, QX, NCB, RPC, KS, kInterior, WM, CT>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
-                                                       lsum);
+            attend<T, QY, QX, NCB, RPC, KS, kInterior, WM, CT, LSE>(a, t, smem, btab, lr, wave, ry, lane, qf,
+                                                            o, lsum, st);
         else
-            attend<T, QY, QX, NCB, RPC, KS, kGeneral, WM, CT>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
-                                                      lsum);
+            attend<T, QY, QX, NCB, RPC, KS, kGeneral, WM, CT, LSE>(a, t, smem, btab, lr, wave, ry, lane, qf,
+                                                           o, lsum, st);
     }
 }
 
 // Normalise and write one wave's 16 outputs: exactly two 16-byte buffer
 // stores per lane, out-of-map queries dropped by the range check.
-template <int QY, int QX>
+// With LSE, lane g == 0 of each query also writes ln(sum of exp(logits)) =
+// (m + log2 sum) ln 2.
+template <int QY, int QX, bool LSE = false>
 __device__ inline void store_out(const Args &a, const Tile &t, int wave, int lane,
-                                 const floatx4 (&o)[2], float lsum)
+                                 const floatx4 (&o)[2], float lsum, const SoftStats &st)
 {
     const int g = lane >> 4, qi = lane & 15;
     const float inv = __builtin_amdgcn_rcpf(quad_sum(lsum));
     const int y = t.y0 + QY * wave + qi / QX;
     const int x = t.x0 + qi % QX;
+    if constexpr (LSE) {
+        const float l = quad_sum(st.l);
+        if (g == 0 && y < a.H && x < a.W)
+            a.lse[t.map_base + (int64_t)y * a.W + x] = (st.m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+    }
     const unsigned off = y < a.H && x < a.W ? (unsigned)(y * a.W + x) * 128u + 16u * g : kOutOfRange;
     const __amdgpu_buffer_rsrc_t ro =
         map_rsrc(a.out, t.map_base, kD * 4, (unsigned)a.H * a.W * (kD * 4));
@@ -547,7 +574,7 @@ __device__ inline void store_out(const Args &a, const Tile &t, int wave, int lan
 // workgroups sharing an L2 work on neighbouring tiles).  Per tile: attend,
 // barrier, issue the next tile's copies, store this tile's outputs, wait for
 // the copies only, barrier.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT, bool LSE = false>
 __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
 {
     using S = Shape<QY, QX, NCB, RPC, kWaves, CT>;
@@ -582,7 +609,8 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
     while (true) {
         floatx4 o[2];
         float lsum;
-        attend_wave<T, QY, QX, NCB, RPC, KS, WM, CT>(a, t, smem, bt, lr, wave, lane, qf, o, lsum);
+        SoftStats st{0.f, 1.f};
+        attend_wave<T, QY, QX, NCB, RPC, KS, WM, CT, LSE>(a, t, smem, bt, lr, wave, lane, qf, o, lsum, st);
         const Tile done = t;
         const unsigned next = tile + step;
         __syncthreads();  // every wave is done reading the LDS copy
@@ -594,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
             }
             stage_tile<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf);
         }
-        store_out<QY, QX>(a, done, wave, lane, o, lsum);
+        store_out<QY, QX, LSE>(a, done, wave, lane, o, lsum, st);
         if (next >= end) break;
         // loads and stores may retire out of order against each other, so
         // only an empty counter proves the copies have landed
@@ -675,7 +703,7 @@ __device__ inline void write_tile_regs(unsigned char *smem, int wave, int lane,
     }
 }
 
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM, bool CT>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM, bool CT, bool LSE = false>
 __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
 {
     using S = Shape<QY, QX, NCB, RPC, NW, CT>;
@@ -724,10 +752,11 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
         // attend from LDS; the next tile is loading into `rg` meanwhile
         floatx4 o[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
         float lsum = 1.f;
+        SoftStats st{0.f, 1.f};
         if (t.y0 + QY * wave < a.H) {  // the bottom tile row may leave whole waves idle
             const FragT qf = __builtin_bit_cast(FragT, *qfrag);
-            attend_wave<T, QY, QX, NCB, RPC, KS, WM, CT>(a, t, halo, btab, LR, wave, lane, qf, o,
-                                                         lsum);
+            attend_wave<T, QY, QX, NCB, RPC, KS, WM, CT, LSE>(a, t, halo, btab, LR, wave, lane, qf, o,
+                                                              lsum, st);
         }
         const Tile done = t;
         const bool more = next < end;
@@ -745,7 +774,7 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
             __builtin_amdgcn_s_waitcnt(0);
             write_tile_regs<QY, QX, NCB, RPC, LR>(halo, wave, lane, rg);
         }
-        store_out<QY, QX>(a, done, wave, lane, o, lsum);
+        store_out<QY, QX, LSE>(a, done, wave, lane, o, lsum, st);
         if (!more) break;
         t = tn;
         tile = next;
@@ -783,6 +812,7 @@ bool make_args(const Problem &p, Args &a)
     a.v = p.v;
     a.rpb = p.rpb;
     a.out = p.out;
+    a.lse = p.lse;
     a.B = p.B;
     a.heads = p.heads;
     a.H = p.H;
@@ -827,7 +857,7 @@ hipError_t launch_persistent(K kern, Args &a, int threads, size_t lds, hipStream
 }
 
 // General kernel sizes: the LDS-DMA kernel with 4 waves per workgroup.
-template <typename T, int QY, int QX, int NCB, int RPC, int WM, bool CT = true, bool FLAT = false>
+template <typename T, int QY, int QX, int NCB, int RPC, int WM, bool LSE, bool CT = true, bool FLAT = false>
 hipError_t launch_dma(const Problem &p, hipStream_t stream)
 {
     using S = Shape<QY, QX, NCB, RPC, kWaves, CT>;
@@ -836,36 +866,39 @@ hipError_t launch_dma(const Problem &p, hipStream_t stream)
     const int nr = wave_rows(QY, RPC, p.ksize);
     const size_t lds =
         lds_bytes(a.lr, S::NC, bias_floats(S::CLS, p.ksize, nr, QY, QX, S::NC, RPC));
-    return launch_persistent(na2d_mfma_kernel<T, QY, QX, NCB, RPC, 0, WM, CT>, a, S::NT, lds,
+    return launch_persistent(na2d_mfma_kernel<T, QY, QX, NCB, RPC, 0, WM, CT, LSE>, a, S::NT, lds,
                              stream, FLAT);
 }
 
 // A compile-time kernel size: the register-prefetch kernel with NW waves.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM, bool CT = true>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int NW, int WM, bool LSE, bool CT = true>
 hipError_t launch_pipe(const Problem &p, hipStream_t stream)
 {
     using S = Shape<QY, QX, NCB, RPC, NW, CT>;
     Args a;
     if (!make_args<S, QY, RPC>(p, a)) return hipErrorInvalidConfiguration;
-    return launch_persistent(na2d_mfma_pipe_kernel<T, QY, QX, NCB, RPC, KS, NW, WM, CT>, a, S::NT, 0,
-                             stream);
+    return launch_persistent(na2d_mfma_pipe_kernel<T, QY, QX, NCB, RPC, KS, NW, WM, CT, LSE>, a, S::NT,
+                             0, stream);
 }
 
-template <typename T, int WM>
+template <typename T, int WM, bool LSE>
 hipError_t launch_typed(const Problem &p, hipStream_t stream)
 {
     const int ks = p.ksize;
-    if (ks == 7) return launch_pipe<T, 2, 8, 1, 8, 7, 4, WM, false>(p, stream);
-    if (ks <= 9) return launch_dma<T, 2, 8, 1, 2, WM>(p, stream);
-    if (ks <= 13) return launch_dma<T, 4, 4, 1, 8, WM>(p, stream);
-    return launch_dma<T, 2, 8, 2, 2, WM>(p, stream);
+    if (ks == 7) return launch_pipe<T, 2, 8, 1, 8, 7, 4, WM, LSE, false>(p, stream);
+    if (ks <= 9) return launch_dma<T, 2, 8, 1, 2, WM, LSE>(p, stream);
+    if (ks <= 13) return launch_dma<T, 4, 4, 1, 8, WM, LSE>(p, stream);
+    return launch_dma<T, 2, 8, 2, 2, WM, LSE>(p, stream);
 }
 
+// The log-sum-exp output exists for NA windows only (it feeds the NA2D backward).
 template <typename T>
 hipError_t launch_mode(const Problem &p, hipStream_t stream)
 {
-    return p.mode == NA_WINDOW_SASA ? launch_typed<T, NA_WINDOW_SASA>(p, stream)
-                                    : launch_typed<T, NA_WINDOW_NA>(p, stream);
+    if (p.mode == NA_WINDOW_SASA)
+        return p.lse ? hipErrorInvalidValue : launch_typed<T, NA_WINDOW_SASA, false>(p, stream);
+    return p.lse ? launch_typed<T, NA_WINDOW_NA, true>(p, stream)
+                 : launch_typed<T, NA_WINDOW_NA, false>(p, stream);
 }
 
 }  // namespace

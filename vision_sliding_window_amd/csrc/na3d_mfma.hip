@@ -49,6 +49,7 @@ struct Args3 {
     const void *q, *k, *v;
     const float *rpb;
     float *out;
+    float *lse;  // per-query log-sum-exp of the logits, or null
     int heads, D, H, W, kd, kh, kw;
     int tiles_x, tiles_yx, tiles_per_map;
     unsigned ntiles;
@@ -240,9 +241,12 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
     if (npairs & 1) process(sa, pa0, pa1, npairs - 1);
 
     // lane (g, c): dims 16 dh + 4 g + r of query c
-    const float inv = 1.f / quad_sum(l);
+    const float lq = quad_sum(l);
+    const float inv = 1.f / lq;
     if (own_valid) {
-        float *dst = a.out + (base + (int64_t)(z * H + qy) * W + qx) * 32 + 4 * g;
+        const int64_t qi = base + (int64_t)(z * H + qy) * W + qx;
+        if (a.lse && g == 0) a.lse[qi] = (m + __builtin_amdgcn_logf(lq)) * 0.6931471805599453f;
+        float *dst = a.out + qi * 32 + 4 * g;
 #pragma unroll
         for (int dh = 0; dh < 2; ++dh) *reinterpret_cast<floatx4 *>(dst + 16 * dh) = o[dh] * inv;
     }
@@ -258,6 +262,7 @@ hipError_t launch_mfma_3d(const Problem &p, hipStream_t stream)
     a.v = p.v;
     a.rpb = p.rpb;
     a.out = p.out;
+    a.lse = p.lse;
     a.heads = p.heads;
     a.D = p.depth;
     a.H = p.H;

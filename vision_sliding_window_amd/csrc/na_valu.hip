@@ -72,7 +72,8 @@ struct Grid {
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void na_valu_kernel(
     const T *__restrict__ q, const T *__restrict__ kk, const T *__restrict__ v,
-    const float *__restrict__ rpb, float *__restrict__ out, Grid g, float c, int64_t nq)
+    const float *__restrict__ rpb, float *__restrict__ out, float *__restrict__ lse, Grid g, float c,
+    int64_t nq)
 {
     // consecutive queries (neighbouring windows) stay on one XCD
     const int64_t gid =
@@ -144,6 +145,7 @@ __global__ __launch_bounds__(256) void na_valu_kernel(
         }
     }
     const float inv = 1.f / l;
+    if (lse) lse[gid] = (m + log2f(l)) * 0.6931471805599453f;  // ln of the sum of exp(logits)
     float4 *dst = reinterpret_cast<float4 *>(out + gid * D);
 #pragma unroll
     for (int e = 0; e < D / 4; ++e)
@@ -161,8 +163,8 @@ hipError_t launch_typed(const Problem &p, hipStream_t stream)
     const Grid g{p.heads, p.depth, p.H, p.W, p.kd, p.kh, p.kw};
     hipLaunchKernelGGL((na_valu_kernel<T, D, MODE>), dim3(static_cast<unsigned>(blocks)),
                        dim3(threads), 0, stream, static_cast<const T *>(p.q),
-                       static_cast<const T *>(p.k), static_cast<const T *>(p.v), p.rpb, p.out, g,
-                       c, nq);
+                       static_cast<const T *>(p.k), static_cast<const T *>(p.v), p.rpb, p.out, p.lse,
+                       g, c, nq);
     return hipGetLastError();
 }
 

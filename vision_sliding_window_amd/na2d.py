@@ -30,7 +30,8 @@ NA2D_ERR_ALIAS = -7
 NA2D_ERR_HIP = -8
 NA2D_ERR_ALGO = -9
 
-EXPORTS = ["na2d_forward", "na2d_forward_ex", "na2d_check_args", "na2d_select_algo",
+EXPORTS = ["na2d_forward", "na2d_forward_ex", "na2d_forward_lse", "na2d_check_args",
+           "na2d_select_algo",
            "na_select_algo_nd",
            "na2d_strerror", "na2d_last_error", "na2d_version", "na_forward_nd",
            "na_check_args_nd", "na1d_forward", "na3d_forward", "sasa2d_forward",
@@ -63,6 +64,8 @@ def load() -> ctypes.CDLL:
         lib.na2d_forward.restype = I
         lib.na2d_forward_ex.argtypes = [P, P, P, P, P] + [I] * 8 + [P]
         lib.na2d_forward_ex.restype = I
+        lib.na2d_forward_lse.argtypes = [P] * 6 + [I] * 7 + [P]
+        lib.na2d_forward_lse.restype = I
         lib.na2d_check_args.argtypes = [P, P, P, P, P] + [I] * 8
         lib.na2d_check_args.restype = I
         lib.na2d_select_algo.argtypes = [I] * 5
@@ -85,11 +88,11 @@ def load() -> ctypes.CDLL:
         lib.na3d_forward.restype = I
         lib.sasa2d_forward.argtypes = [P, P, P, P, P] + [I] * 7 + [P]
         lib.sasa2d_forward.restype = I
-        lib.na2d_backward.argtypes = [P] * 11 + [I] * 7 + [P]
+        lib.na2d_backward.argtypes = [P] * 12 + [I] * 7 + [P]
         lib.na2d_backward.restype = I
         lib.na2d_backward_workspace_bytes.argtypes = [I] * 5
         lib.na2d_backward_workspace_bytes.restype = ctypes.c_longlong
-        lib.na2d_backward_check_args.argtypes = [P] * 11 + [I] * 7
+        lib.na2d_backward_check_args.argtypes = [P] * 12 + [I] * 7
         lib.na2d_backward_check_args.restype = I
         _lib = lib
     return _lib
@@ -120,6 +123,12 @@ def na2d_forward_ex(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, algo,
                     stream=None) -> int:
     return load().na2d_forward_ex(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out),
                                   B, heads, H, W, d, ksize, dtype, algo, _stream(stream))
+
+
+def na2d_forward_lse(q, k, v, rpb, out, lse, B, heads, H, W, d, ksize, dtype,
+                     stream=None) -> int:
+    return load().na2d_forward_lse(_addr(q), _addr(k), _addr(v), _addr(rpb), _addr(out),
+                                   _addr(lse), B, heads, H, W, d, ksize, dtype, _stream(stream))
 
 
 def na2d_check_args(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, algo) -> int:
@@ -164,10 +173,10 @@ def sasa2d_forward(q, k, v, rpb, out, B, heads, H, W, d, ksize, dtype, stream=No
                                  H, W, d, ksize, dtype, _stream(stream))
 
 
-def na2d_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads, H, W, d, ksize,
-                  dtype, stream=None) -> int:
-    return load().na2d_backward(*(_addr(t) for t in (q, k, v, rpb, out, dout, dq, dk, dv, drpb,
-                                                     workspace)),
+def na2d_backward(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, workspace, B, heads, H, W, d,
+                  ksize, dtype, stream=None) -> int:
+    return load().na2d_backward(*(_addr(t) for t in (q, k, v, rpb, out, lse, dout, dq, dk, dv,
+                                                     drpb, workspace)),
                                 B, heads, H, W, d, ksize, dtype, _stream(stream))
 
 
@@ -175,10 +184,10 @@ def na2d_backward_workspace_bytes(B, heads, H, W, ksize) -> int:
     return load().na2d_backward_workspace_bytes(B, heads, H, W, ksize)
 
 
-def na2d_backward_check_args(q, k, v, rpb, out, dout, dq, dk, dv, drpb, workspace, B, heads, H, W,
-                             d, ksize, dtype) -> int:
-    return load().na2d_backward_check_args(*(_addr(t) for t in (q, k, v, rpb, out, dout, dq, dk,
-                                                                dv, drpb, workspace)),
+def na2d_backward_check_args(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, workspace, B, heads,
+                             H, W, d, ksize, dtype) -> int:
+    return load().na2d_backward_check_args(*(_addr(t) for t in (q, k, v, rpb, out, lse, dout, dq,
+                                                                dk, dv, drpb, workspace)),
                                            B, heads, H, W, d, ksize, dtype)
 
 
@@ -221,6 +230,22 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rpb, ksize: int,
     if st != NA2D_OK:
         raise NA2DError(st, na2d_last_error() if st == NA2D_ERR_HIP else "")
     return out
+
+
+def forward_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rpb, ksize: int, stream=None):
+    """The training forward: (out, lse) with lse [B, heads, H, W] float32 the
+    log-sum-exp of each query's logits, for ``backward(..., lse=lse)``."""
+    _check_inputs(q, k, v, rpb, 5, (q.shape[1], 2 * ksize - 1, 2 * ksize - 1))
+    B, heads, H, W, d = q.shape
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:4], dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = na2d_forward_lse(q, k, v, rpb, out, lse, B, heads, H, W, d, ksize,
+                          TORCH_DTYPE_CODE[q.dtype], stream)
+    if st != NA2D_OK:
+        raise NA2DError(st, na2d_last_error() if st == NA2D_ERR_HIP else "")
+    return out, lse
 
 
 def _check_inputs(q, k, v, rpb, ndim, rpb_shape):
@@ -291,11 +316,11 @@ def forward_nd(q, k, v, rpb, window, mode=NA_WINDOW_NA, algo=NA2D_ALGO_AUTO, out
     return out
 
 
-def backward(q, k, v, rpb, out, dout, ksize: int, stream=None):
+def backward(q, k, v, rpb, out, dout, ksize: int, stream=None, lse=None):
     """Gradients (dq, dk, dv, drpb) of the NA2D forward on device tensors: q, k,
     v, rpb as for ``forward``, out its float32 output, dout float32 of out's
-    shape.  drpb is None when rpb is None.  Allocates the outputs and the
-    workspace with torch."""
+    shape, lse (optional) the log-sum-exp from ``forward_lse``.  drpb is None
+    when rpb is None.  Allocates the outputs and the workspace with torch."""
     for t in (q, k, v):
         if not (t.is_cuda and t.is_contiguous() and t.dim() == 5):
             raise ValueError("q, k, v must be contiguous 5-d GPU tensors [B, heads, H, W, d]")
@@ -309,8 +334,11 @@ def backward(q, k, v, rpb, out, dout, ksize: int, stream=None):
     ws = torch.empty(max(1, na2d_backward_workspace_bytes(B, heads, H, W, ksize) // 4), **f32)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = na2d_backward(q, k, v, rpb, out, dout, dq, dk, dv, drpb, ws, B, heads, H, W, d, ksize,
-                       TORCH_DTYPE_CODE[q.dtype], stream)
+    if lse is not None and not (lse.is_cuda and lse.is_contiguous() and lse.dtype == torch.float32
+                                and lse.shape == q.shape[:4]):
+        raise ValueError("lse must be a contiguous float32 GPU tensor [B, heads, H, W]")
+    st = na2d_backward(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, ws, B, heads, H, W, d,
+                       ksize, TORCH_DTYPE_CODE[q.dtype], stream)
     if st != NA2D_OK:
         raise NA2DError(st, na2d_last_error() if st == NA2D_ERR_HIP else "")
     return dq, dk, dv, drpb
