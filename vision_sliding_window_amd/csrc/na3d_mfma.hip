@@ -9,13 +9,16 @@
 // window, weighted sum of the values.
 //
 // How.  A workgroup owns an 8 x 8 patch of queries at one depth z; each of
-// its four waves owns 2 rows x 8 columns (16 queries).  All of a wave's
-// queries share z and so the depth slices of their windows; the wave walks
-// the 16-key blocks (one key row, 16 consecutive columns) that cover the
-// union of their windows -- kd slices x (kh + 1) rows x one block for
-// windows up to 9 wide -- straight from L2, two blocks at a time:
+// its four waves owns a QY x QX = 16-query subtile.  All of a wave's queries
+// share z and so the depth slices of their windows; the wave walks the
+// 16-key blocks (BR key rows x 16/BR consecutive columns) that cover the
+// union of their windows, straight from L2, two blocks at a time.  Two
+// shapes: 2 x 8 queries against 1 x 16 key blocks (kd slices x (kh + 1) rows
+// x one block for windows up to 9 wide), and, for windows up to 5 wide,
+// 4 x 4 queries against 2 x 8 key blocks (kd slices x (kh + 3) / 2 row pairs
+// x one block: a third fewer blocks at k = 5).  Per pair of blocks:
 //  - S^T = K_block Q^T, one v_mfma_f32_16x16x32 per block: lane (g, c)
-//    holds query c against keys 4g..4g+3 of the block;
+//    holds query c against keys 4g..4g+3 of the block (one key row);
 //  - the bias (times log2(e)/sqrt(d)) comes from an LDS copy of the head's
 //    table; keys outside a query's window are masked to -inf;
 //  - online softmax over the pair: one max over the four lanes of a query
@@ -63,29 +66,32 @@ __device__ inline int wstart3(int i, int ks, int L)
     return s > L - ks ? L - ks : s;
 }
 
-// The 16-byte d-slice g of the 16-bit row of pixel (z, y, x) of the map
-// (lane (g, i) of a block takes x = x0 + i); zeros past the map's last column.
+// The 16-byte d-slice g of the 16-bit row of pixel (z, y, x) of the map;
+// zeros for a pixel past the map's last row or column.
 __device__ inline u32x4 load_slice3(__amdgpu_buffer_rsrc_t r, int z, int y, int x, int H, int W, int g)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(
-        r, x < W ? (unsigned)((z * H + y) * W + x) * 64u + 16u * (unsigned)g : kOutOfRange, 0, 0);
+        r, x < W && y < H ? (unsigned)((z * H + y) * W + x) * 64u + 16u * (unsigned)g : kOutOfRange,
+        0, 0);
 }
 
-// Walks the key blocks of a wave (slices z0.., rows y0..y1, nblk column
-// blocks from x0) one at a time; past the last block it stays on the last.
+// Walks the key blocks of a wave one at a time: slices z0..zlast, block rows
+// y0, y0 + BR, .. up to y1, nblk column blocks of width BC from x0; past the
+// last block it stays on the last.
+template <int BR, int BC>
 struct Walk3 {
     int z, y, b;
     int zlast;
     const int y0, y1, x0, nblk;
     __device__ Walk3(int z0, int zl, int y0_, int y1_, int x0_, int nblk_)
         : z(z0), y(y0_), b(0), zlast(zl), y0(y0_), y1(y1_), x0(x0_), nblk(nblk_) {}
-    __device__ int xb() const { return x0 + 16 * b; }
+    __device__ int xb() const { return x0 + BC * b; }
     __device__ void advance()
     {
         if (++b < nblk) return;
         b = 0;
-        if (y < y1) {
-            ++y;
+        if (y + BR <= y1) {
+            y += BR;
         } else if (z < zlast) {
             ++z;
             y = y0;
@@ -99,9 +105,12 @@ struct Pos {
     int z, y, xb;
 };
 
-template <typename T>
+// QY x QX: a wave's queries; BR x BC (= 16): a key block.
+template <typename T, int QY, int QX, int BR>
 __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
 {
+    constexpr int BC = 16 / BR;
+    static_assert(QY * QX == 16 && BR * BC == 16 && 4 % BR == 0 && 8 % QX == 0, "shape");
     using FragT = typename Frag<T>::type;
     __shared__ float table[kPad + kMaxTable + kPad];              // bias table, times c, with margins
     float *const raw = table + kPad;
@@ -127,10 +136,11 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
 
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int qy1 = y0 + 2 * wave;  // the wave's query rows qy1, qy1 + 1
-    if (qy1 >= H) return;
-    const int qy = min(qy1 + (c >> 3), H - 1), qx = min(x0 + (c & 7), W - 1);
-    const bool own_valid = qy1 + (c >> 3) < H && x0 + (c & 7) < W;
+    // the wave's subtile: rows qy1 .. qy1 + QY - 1, columns qx1 .. qx1 + QX - 1
+    const int qy1 = y0 + QY * (wave / (8 / QX)), qx1 = x0 + QX * (wave % (8 / QX));
+    if (qy1 >= H || qx1 >= W) return;
+    const int qy = min(qy1 + c / QX, H - 1), qx = min(qx1 + c % QX, W - 1);
+    const bool own_valid = qy1 + c / QX < H && qx1 + c % QX < W;
     const int sy = wstart3(qy, kh, H), sx = wstart3(qx, kw, W), sz = wstart3(z, kd, D);
     const int64_t base = (int64_t)map * D * H * W;
     const unsigned map_bytes = (unsigned)D * H * W * 64u;
@@ -142,10 +152,10 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
         FragT, __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)((z * H + qy) * W + qx) * 64u + 16u * g, 0, 0));
 
     // key blocks the wave's windows touch
-    const int kylo = wstart3(qy1, kh, H), kyhi = wstart3(min(qy1 + 1, H - 1), kh, H) + kh - 1;
-    const int kxlo = wstart3(x0, kw, W), kxhi = wstart3(min(x0 + 7, W - 1), kw, W) + kw - 1;
-    const int nblk = (kxhi - kxlo + 16) >> 4;
-    const int nblocks = kd * (kyhi - kylo + 1) * nblk;
+    const int kylo = wstart3(qy1, kh, H), kyhi = wstart3(min(qy1 + QY - 1, H - 1), kh, H) + kh - 1;
+    const int kxlo = wstart3(qx1, kw, W), kxhi = wstart3(min(qx1 + QX - 1, W - 1), kw, W) + kw - 1;
+    const int nblk = (kxhi - kxlo + BC) / BC;
+    const int nblocks = kd * ((kyhi - kylo + BR) / BR) * nblk;
     const int npairs = (nblocks + 1) >> 1;
 
     float m = -1e30f, l = 0.f;  // running max (shared by a query's 4 lanes) and this lane's sum
@@ -155,18 +165,21 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
     const unsigned st_off = stage_off(g, c);
     const int zoff = z - (kd - 1);  // key slice minus this, times the row stride, indexes the table
 
-    // logits of block (p.z, p.y, p.xb) for query c, keys 4g + r, in log2 units.
+    // logits of block (p.z, p.y, p.xb) for query c, keys 4g + r, in log2 units:
+    // key 4g + r of the block is (row p.y + 4g / BC, column p.xb + 4g % BC + r).
     // The four bias entries are read unconditionally from a base clamped into
     // the padded table (a masked key's entry is never used), so the reads
     // need no branches.
     const int nmax = nbd * nbh * nbw;
+    const int krow = 4 * g / BC, kcol = 4 * g % BC;  // this lane's keys within a block
     auto logits = [&](const floatx4 &s, const Pos &p, bool real, float *t) {
-        const bool rowin = real && own_valid && (unsigned)(p.y - sy) < (unsigned)kh;
-        const int base = ((p.z - zoff) * nbh + (p.y - qy + kh - 1)) * nbw + p.xb + 4 * g - qx + kw - 1;
+        const int ky = p.y + krow;
+        const bool rowin = real && own_valid && (unsigned)(ky - sy) < (unsigned)kh;
+        const int base = ((p.z - zoff) * nbh + (ky - qy + kh - 1)) * nbw + p.xb + kcol - qx + kw - 1;
         const float *bp = raw + min(max(base, -kPad), nmax + kPad - 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int kx = p.xb + 4 * g + r;
+            const int kx = p.xb + kcol + r;
             const bool in = rowin && (unsigned)(kx - sx) < (unsigned)kw;
             float b = bp[r];
             asm volatile("" : "+v"(b));  // keeps the read out of a branch on `in`
@@ -176,16 +189,18 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
     struct Pair {
         u32x4 k0, v0, k1, v1;
     };
-    Walk3 walk(sz, sz + kd - 1, kylo, kyhi, kxlo, nblk);
+    Walk3<BR, BC> walk(sz, sz + kd - 1, kylo, kyhi, kxlo, nblk);
+    // lane (g, c) loads slice g of key c of a block: (row + c / BC, column + c % BC)
+    const int lrow = c / BC, lcol = c % BC;
     auto load_pair = [&](Pos &p0, Pos &p1) {
         Pair t;
         p0 = Pos{walk.z, walk.y, walk.xb()};
-        t.k0 = load_slice3(rk, p0.z, p0.y, p0.xb + c, H, W, g);
-        t.v0 = load_slice3(rv, p0.z, p0.y, p0.xb + c, H, W, g);
+        t.k0 = load_slice3(rk, p0.z, p0.y + lrow, p0.xb + lcol, H, W, g);
+        t.v0 = load_slice3(rv, p0.z, p0.y + lrow, p0.xb + lcol, H, W, g);
         walk.advance();
         p1 = Pos{walk.z, walk.y, walk.xb()};
-        t.k1 = load_slice3(rk, p1.z, p1.y, p1.xb + c, H, W, g);
-        t.v1 = load_slice3(rv, p1.z, p1.y, p1.xb + c, H, W, g);
+        t.k1 = load_slice3(rk, p1.z, p1.y + lrow, p1.xb + lcol, H, W, g);
+        t.v1 = load_slice3(rv, p1.z, p1.y + lrow, p1.xb + lcol, H, W, g);
         walk.advance();
         return t;
     };
@@ -278,12 +293,22 @@ hipError_t launch_mfma_3d(const Problem &p, hipStream_t stream)
     if (tiles == 0 || xcd_grid(tiles) > 0x7fffffffull) return hipErrorInvalidConfiguration;
     a.ntiles = (unsigned)tiles;
     const dim3 grid((unsigned)xcd_grid(tiles));
-    if (p.dtype == NA2D_F16)
-        hipLaunchKernelGGL(na3d_mfma_kernel<_Float16>, grid, dim3(kT3), 0, stream, a);
-    else if (p.dtype == NA2D_BF16)
-        hipLaunchKernelGGL(na3d_mfma_kernel<__bf16>, grid, dim3(kT3), 0, stream, a);
-    else
+    // 4 x 4 query subtiles against 2-row key blocks when a window's columns
+    // for 4 queries fit in 8 (kw <= 5), else 2 x 8 against 1-row blocks
+    const bool narrow = p.kw <= 5;
+    if (p.dtype == NA2D_F16) {
+        if (narrow)
+            hipLaunchKernelGGL((na3d_mfma_kernel<_Float16, 4, 4, 2>), grid, dim3(kT3), 0, stream, a);
+        else
+            hipLaunchKernelGGL((na3d_mfma_kernel<_Float16, 2, 8, 1>), grid, dim3(kT3), 0, stream, a);
+    } else if (p.dtype == NA2D_BF16) {
+        if (narrow)
+            hipLaunchKernelGGL((na3d_mfma_kernel<__bf16, 4, 4, 2>), grid, dim3(kT3), 0, stream, a);
+        else
+            hipLaunchKernelGGL((na3d_mfma_kernel<__bf16, 2, 8, 1>), grid, dim3(kT3), 0, stream, a);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
