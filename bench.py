@@ -122,9 +122,46 @@ def cpu_baseline(w, x, seconds: float = 10.0):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    # a per-core figure: one thread on a smaller sample, about a tenth of the time
+    n1 = int(min(n, max(64, rate / cores * seconds / 10)))
+    t1 = time.perf_counter()
+    if w.op == "na2d":
+        oracle.na2d_forward_sampled(x.q64, x.k64, x.v64, x.rpb64, w.k, sample[:n1], nthreads=1)
+    else:
+        ref(x.q64, x.k64, x.v64, x.rpb64, w.k, idx=sample[:n1], nthreads=1)
+    one = n1 / max(time.perf_counter() - t1, 1e-6)
     return {"value": done / el, "unit": "queries/s", "cores": cores, "kind": "oracle",
             "sample": "%d random queries of %s (seed 1), %d pass(es), fp64, %.1f s"
-                      % (n, w.name, done // n, el)}
+                      % (n, w.name, done // n, el),
+            "cpu_model": cpu_model(), "one_thread_value": round(one, 1)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def d2d_copy_gbs(torch, dev, nbytes: int = 2 ** 30, reps: int = 10) -> float:
+    """Read + write rate of a plain device-to-device copy of nbytes on this GPU."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def backward_bytes(w, with_lse: bool = False) -> int:
@@ -241,8 +278,12 @@ def main():
     ap.add_argument("--algo", default="auto", choices=sorted(ALGOS))
     ap.add_argument("--min-footprint-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hot", action="store_true",
+                    help="skip the cache-resident (single-set) timing")
+    ap.add_argument("--q-scale", type=float, default=1.0,
+                    help="stress: Q times this (peaked softmax); 1 is the graded input")
     ap.add_argument("--hot", action="store_true",
-                    help="also time one cache-resident input set (reported separately)")
+                    help="(the default) also time one cache-resident input set, reported separately")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--recompute-stats", action="store_true",
                     help="--backward without the forward's log-sum-exp (the backward recomputes it)")
@@ -294,7 +335,7 @@ def main():
             sys.exit(2)
         return bench_backward(args, w, wname, lib, dev, dtype_code)
 
-    x = workload_inputs(w, seed=0)
+    x = workload_inputs(w, seed=0, q_scale=args.q_scale)
     set_bytes = algorithmic_bytes(w)
     nsets = max(1, math.ceil(args.min_footprint_gib * 2 ** 30 / set_bytes))
     q0, k0, v0 = x.q.to(dev), x.k.to(dev), x.v.to(dev)
@@ -332,7 +373,7 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     hot_ms = None
-    if args.hot:  # cache-resident figure (one set, L2/MALL hits), labelled as such
+    if not args.no_hot:  # cache-resident figure (one set, L2/MALL hits), labelled as such
         hs = torch.cuda.Event(enable_timing=True)
         he = torch.cuda.Event(enable_timing=True)
         hs.record(stream)
@@ -342,6 +383,7 @@ def main():
         torch.cuda.synchronize()
         hot_ms = hs.elapsed_time(he) / args.steps
 
+    copy_gbs = d2d_copy_gbs(torch, dev)
     value = w.queries / (ms * 1e-3)
     gbs = set_bytes / (ms * 1e-3) / 1e9
     tflops = algorithmic_flops(w) / (ms * 1e-3) / 1e12
@@ -362,13 +404,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic: Q,K,V ~ N(0,1), RPB ~ N(0,0.02), seed 0",
+        "data": "synthetic: Q,K,V ~ N(0,1), RPB ~ N(0,0.02), seed 0" +
+                ("" if args.q_scale == 1.0 else "; stress: Q x %g (not graded)" % args.q_scale),
         "config": {"workload": wname, "op": w.op, "B": w.B, "heads": w.heads, "D": w.depth,
                    "H": w.H, "W": w.W, "d": w.d, "k": w.k, "kernel": algo_name,
                    "rotating_sets": nsets,
                    "footprint_bytes": nsets * set_bytes, "algorithmic_bytes_per_step": set_bytes,
                    "hot_ms_per_step": None if hot_ms is None else round(hot_ms, 6),
-                   "useful_tflops": round(tflops, 2)},
+                   "useful_tflops": round(tflops, 2),
+                   "d2d_copy_gbs": round(copy_gbs, 1),
+                   "frac_of_d2d_copy": round(gbs / copy_gbs, 4),
+                   "q_scale": args.q_scale},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
