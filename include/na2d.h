@@ -90,8 +90,9 @@ enum {
 #define NA2D_MFMA_MAX_KSIZE 25
 /* Largest window of the NA1D matrix-core kernel (d = 32, 16-bit inputs). */
 #define NA1D_MFMA_MAX_KSIZE 63
-/* Largest window per axis of the matrix-core kernel for 3D windows and
- * rectangular 2D windows (d = 32, 16-bit inputs, NA). */
+/* Largest window per axis of the streaming matrix-core kernel for 3D windows
+ * (d = 32, 16-bit inputs, NA); its 2D windows (kd = 1) go up to
+ * NA2D_MFMA_MAX_KSIZE. */
 #define NA3D_MFMA_MAX_KSIZE 9
 /* Largest window whose backward runs on the matrix cores (d = 32, 16-bit
  * inputs); larger windows, fp32 and other head dims use the VALU kernels. */
@@ -152,8 +153,9 @@ int na2d_select_algo(int H, int W, int d, int ksize, int dtype);
  * kernels serve 16-bit inputs with d = 32 in three shapes: square 2D windows
  * (D = 1, kd = 1, kh = kw, 3 <= kh <= NA2D_MFMA_MAX_KSIZE), NA or SASA;
  * NA1D (D = H = 1, kd = kh = 1, 3 <= kw <= NA1D_MFMA_MAX_KSIZE, NA); and any
- * other NA window (3D, or rectangular 2D) with every axis at most
- * NA3D_MFMA_MAX_KSIZE.  AUTO picks them wherever they apply. */
+ * other NA window: 3D windows with every axis at most NA3D_MFMA_MAX_KSIZE,
+ * 2D windows (rectangular, or square and wider than 13) up to
+ * NA2D_MFMA_MAX_KSIZE.  AUTO picks them wherever they apply. */
 int na_forward_nd(const void *q, const void *k, const void *v, const float *rpb, float *out,
                   int B, int heads, int D, int H, int W, int d, int kd, int kh, int kw,
                   int mode, int dtype, int algo, void *stream);

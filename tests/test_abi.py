@@ -153,6 +153,12 @@ def test_select_algo():
     assert na2d.na_select_algo_nd(4, 9, 9, 32, (3, 3, 3), NA, na2d.NA2D_F32) == na2d.NA2D_ALGO_VALU
     assert na2d.na_select_algo_nd(4, 9, 9, 32, (3, 3, 3), 7, f16) == na2d.NA2D_ERR_UNSUPPORTED
     assert na2d.na_select_algo_nd(4, 9, 9, 32, (11, 3, 3), NA, f16) == na2d.NA2D_ERR_KSIZE
+    # wide 2D windows: NA on the streaming kernel, SASA on the halo kernel, both MFMA
+    assert na2d.na_select_algo_nd(1, 64, 64, 32, (1, 21, 21), NA, f16) == na2d.NA2D_ALGO_MFMA
+    assert na2d.na_select_algo_nd(1, 64, 64, 32, (1, 21, 21), SASA, f16) == na2d.NA2D_ALGO_MFMA
+    assert na2d.na_select_algo_nd(1, 64, 64, 32, (1, 25, 9), NA, f16) == na2d.NA2D_ALGO_MFMA
+    assert na2d.na_select_algo_nd(1, 64, 64, 32, (1, 27, 27), NA, f16) == na2d.NA2D_ALGO_VALU
+    assert na2d.na_select_algo_nd(12, 64, 64, 32, (3, 11, 3), NA, f16) == na2d.NA2D_ALGO_VALU
     assert na2d.na2d_select_algo(14, 14, 32, 8, na2d.NA2D_F16) == na2d.NA2D_ERR_KSIZE
 
 

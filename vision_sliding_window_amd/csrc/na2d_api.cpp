@@ -42,20 +42,29 @@ bool is_mfma_1d(const Nd &n)
            n.kw >= 3 && n.kw <= NA1D_MFMA_MAX_KSIZE;
 }
 
-// The 2D matrix-core kernel: square windows (NA or SASA).
+// The 2D matrix-core kernel (a K/V halo per tile in LDS): square windows, NA
+// up to k = 13 and SASA up to NA2D_MFMA_MAX_KSIZE.  Wider NA windows go to
+// the streaming kernel below: their halos fill the LDS and leave one or two
+// workgroups per CU, and the streaming kernel runs k = 15..25 about 35%
+// faster.
+constexpr int kHaloMaxNaK = 13;
+
 bool is_mfma_2d(const Nd &n)
 {
-    return n.D == 1 && n.kd == 1 && n.kh == n.kw && n.kh >= 3 && n.kh <= NA2D_MFMA_MAX_KSIZE;
+    return n.D == 1 && n.kd == 1 && n.kh == n.kw && n.kh >= 3 && n.kh <= NA2D_MFMA_MAX_KSIZE &&
+           (n.mode == NA_WINDOW_SASA || n.kh <= kHaloMaxNaK);
 }
 
 // Both take 16-bit inputs with d = 32 and address one (b, h) map with 32-bit
 // byte offsets.
-// Any other NA window with every axis small enough: 3D windows and the
-// rectangular 2D ones.
+// The streaming kernel: any other NA window with every axis small enough --
+// 3D windows up to NA3D_MFMA_MAX_KSIZE per axis, 2D windows (kd = 1, square
+// or rectangular) up to NA2D_MFMA_MAX_KSIZE.
 bool is_mfma_3d(const Nd &n)
 {
-    return !is_mfma_1d(n) && !is_mfma_2d(n) && n.mode == NA_WINDOW_NA &&
-           n.kd <= NA3D_MFMA_MAX_KSIZE && n.kh <= NA3D_MFMA_MAX_KSIZE && n.kw <= NA3D_MFMA_MAX_KSIZE;
+    if (is_mfma_1d(n) || is_mfma_2d(n) || n.mode != NA_WINDOW_NA) return false;
+    const int lim = n.kd == 1 ? NA2D_MFMA_MAX_KSIZE : NA3D_MFMA_MAX_KSIZE;
+    return n.kd <= NA3D_MFMA_MAX_KSIZE && n.kh <= lim && n.kw <= lim;
 }
 
 bool mfma_supports(const Nd &n, int dtype)

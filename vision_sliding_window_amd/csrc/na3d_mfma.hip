@@ -44,8 +44,12 @@ namespace {
 
 constexpr int kW3 = 4;          // waves per workgroup
 constexpr int kT3 = 64 * kW3;   // threads per workgroup
-constexpr int kMaxTable =
+// the largest bias table: a 3D window of NA3D_MFMA_MAX_KSIZE per axis, or a 2D
+// one of NA2D_MFMA_MAX_KSIZE
+constexpr int kTable3 =
     (2 * NA3D_MFMA_MAX_KSIZE - 1) * (2 * NA3D_MFMA_MAX_KSIZE - 1) * (2 * NA3D_MFMA_MAX_KSIZE - 1);
+constexpr int kTable2 = (2 * NA2D_MFMA_MAX_KSIZE - 1) * (2 * NA2D_MFMA_MAX_KSIZE - 1);
+constexpr int kMaxTable = kTable3 > kTable2 ? kTable3 : kTable2;
 constexpr int kPad = 16;  // floats of margin before and after the bias table
 
 struct Args3 {
@@ -271,6 +275,9 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
 
 hipError_t launch_mfma_3d(const Problem &p, hipStream_t stream)
 {
+    if (p.d != 32 || p.mode != NA_WINDOW_NA ||
+        (2 * p.kd - 1) * (2 * p.kh - 1) * (2 * p.kw - 1) > kMaxTable)
+        return hipErrorInvalidValue;
     Args3 a;
     a.q = p.q;
     a.k = p.k;
