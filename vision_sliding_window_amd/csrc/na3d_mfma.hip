@@ -12,11 +12,11 @@
 // its four waves owns a QY x QX = 16-query subtile.  All of a wave's queries
 // share z and so the depth slices of their windows; the wave walks the
 // 16-key blocks (BR key rows x 16/BR consecutive columns) that cover the
-// union of their windows, straight from L2, two blocks at a time.  Two
-// shapes: 2 x 8 queries against 1 x 16 key blocks (kd slices x (kh + 1) rows
-// x one block for windows up to 9 wide), and, for windows up to 5 wide,
-// 4 x 4 queries against 2 x 8 key blocks (kd slices x (kh + 3) / 2 row pairs
-// x one block: a third fewer blocks at k = 5).  Per pair of blocks:
+// union of their windows, straight from L2, two blocks at a time.  Three
+// shapes -- 2 x 8 queries against 1 x 16 key blocks, 4 x 4 queries against
+// 2 x 8 or 4 x 4 blocks -- and each launch takes the one with the fewest
+// blocks per slice for its window (at k = 5: 4 instead of 6; at k = 21: 36
+// instead of 44).  Per pair of blocks:
 //  - S^T = K_block Q^T, one v_mfma_f32_16x16x32 per block: lane (g, c)
 //    holds query c against keys 4g..4g+3 of the block (one key row);
 //  - the bias (times log2(e)/sqrt(d)) comes from an LDS copy of the head's
@@ -273,6 +273,23 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
 
 }  // namespace
 
+namespace {
+
+// shape 0: 2 x 8 queries, 1 x 16 key blocks; 1: 4 x 4 queries, 2 x 8 blocks;
+// 2: 4 x 4 queries, 4 x 4 blocks
+template <typename T>
+void launch_shape(int shape, dim3 grid, const Args3 &a, hipStream_t stream)
+{
+    if (shape == 0)
+        hipLaunchKernelGGL((na3d_mfma_kernel<T, 2, 8, 1>), grid, dim3(kT3), 0, stream, a);
+    else if (shape == 1)
+        hipLaunchKernelGGL((na3d_mfma_kernel<T, 4, 4, 2>), grid, dim3(kT3), 0, stream, a);
+    else
+        hipLaunchKernelGGL((na3d_mfma_kernel<T, 4, 4, 4>), grid, dim3(kT3), 0, stream, a);
+}
+
+}  // namespace
+
 hipError_t launch_mfma_3d(const Problem &p, hipStream_t stream)
 {
     if (p.d != 32 || p.mode != NA_WINDOW_NA ||
@@ -300,22 +317,20 @@ hipError_t launch_mfma_3d(const Problem &p, hipStream_t stream)
     if (tiles == 0 || xcd_grid(tiles) > 0x7fffffffull) return hipErrorInvalidConfiguration;
     a.ntiles = (unsigned)tiles;
     const dim3 grid((unsigned)xcd_grid(tiles));
-    // 4 x 4 query subtiles against 2-row key blocks when a window's columns
-    // for 4 queries fit in 8 (kw <= 5), else 2 x 8 against 1-row blocks
-    const bool narrow = p.kw <= 5;
-    if (p.dtype == NA2D_F16) {
-        if (narrow)
-            hipLaunchKernelGGL((na3d_mfma_kernel<_Float16, 4, 4, 2>), grid, dim3(kT3), 0, stream, a);
-        else
-            hipLaunchKernelGGL((na3d_mfma_kernel<_Float16, 2, 8, 1>), grid, dim3(kT3), 0, stream, a);
-    } else if (p.dtype == NA2D_BF16) {
-        if (narrow)
-            hipLaunchKernelGGL((na3d_mfma_kernel<__bf16, 4, 4, 2>), grid, dim3(kT3), 0, stream, a);
-        else
-            hipLaunchKernelGGL((na3d_mfma_kernel<__bf16, 2, 8, 1>), grid, dim3(kT3), 0, stream, a);
-    } else {
+    // the subtile / block shape with the fewest key blocks per wave and depth
+    // slice: ceil((QY + kh - 1) / BR) * ceil((QX + kw - 1) / BC)
+    auto blocks = [&](int qy, int qx, int br) {
+        const int bc = 16 / br;
+        return ((qy + p.kh - 1 + br - 1) / br) * ((qx + p.kw - 1 + bc - 1) / bc);
+    };
+    const int nA = blocks(2, 8, 1), nB = blocks(4, 4, 2), nD = blocks(4, 4, 4);
+    const int shape = nA <= nB && nA <= nD ? 0 : nB <= nD ? 1 : 2;
+    if (p.dtype == NA2D_F16)
+        launch_shape<_Float16>(shape, grid, a, stream);
+    else if (p.dtype == NA2D_BF16)
+        launch_shape<__bf16>(shape, grid, a, stream);
+    else
         return hipErrorInvalidValue;
-    }
     return hipGetLastError();
 }
 
