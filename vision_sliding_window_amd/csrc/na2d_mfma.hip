@@ -44,6 +44,7 @@
 #include "na2d.h"
 #include "na2d_launch.h"
 #include "na_mfma_util.h"
+#include "na_xcd.h"
 
 #include <hip/hip_runtime.h>
 
@@ -81,6 +82,10 @@ struct Args {
     int lr;                // halo rows held in LDS
     int xcd_split;         // 1: tiles split into 8 contiguous ranges, one per XCD
     float c;               // log2(e) / sqrt(d)
+    // column runs (na2d_mfma_ring_kernel): run r covers tile rows
+    // [part * run_len, ...) of tile column r / runs_per_col, part = r % runs_per_col
+    unsigned nruns;
+    int runs_per_col, run_len;
 };
 
 template <int QY, int QX, int NCB, int RPC, int NW = kWaves, bool CT = true>
@@ -321,7 +326,10 @@ struct SoftStats {
     float m, l;
 };
 
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int MODE, int WM, bool CT, bool LSE = false>
+// RING > 0: the halo is a ring of RING rows in which map row gy sits at slot
+// gy & (RING - 1) (see na2d_mfma_ring_kernel); 0: halo row i at LDS row i.
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int MODE, int WM, bool CT, bool LSE = false,
+          int RING = 0>
 __device__ inline void attend(const Args &a, const Tile &t, const unsigned char *smem,
                               const float *btab, int lr, int wave, int ry, int lane,
                               const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum,
@@ -338,7 +346,9 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
     const int qy = qi / QX, qx = qi % QX;
     const int y = min(t.y0 + QY * wave + qy, H - 1);
     const int x = min(t.x0 + qx, W - 1);
-    const int rrel = ry - t.hy0;
+    const int rrel = RING ? 0 : ry - t.hy0;
+    // LDS row of candidate row r of chunk c0 (a uniform value)
+    auto slot = [&](int c0, int r) { return RING ? ((ry + c0 + r) & (RING - 1)) : r; };
 
     // K block row: 16 lanes read 16 columns' d-slice g (swizzled slot)
     lds_cu8 *kp = (lds_cu8 *)(smem + (unsigned)(rrel * S::NC) * 64u + (unsigned)qi * 64u +
@@ -392,6 +402,17 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 
     for (int c0 = 0; c0 < nr; c0 += RPC) {
         float sc[RPC][NCB][4];
+        // with a ring the row addresses are computed, and the chunk's K rows
+        // are read up front so that the reads overlap
+        FragT kring[RING ? RPC : 1][NCB];
+        if constexpr (RING) {
+#pragma unroll
+            for (int rr = 0; rr < RPC; ++rr)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    kring[rr][cb] = __builtin_bit_cast(
+                        FragT, *(lds_cu4 *)(kp + (slot(c0, rr) * S::NC + 16 * cb) * 64));
+        }
 #pragma unroll
         for (int rr = 0; rr < RPC; ++rr) {
             lds_cf32 *brow;
@@ -410,7 +431,8 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const FragT kf =
-                    __builtin_bit_cast(FragT, *(lds_cu4 *)(kp + (rr * S::NC + 16 * cb) * 64));
+                    RING ? kring[RING ? rr : 0][cb]
+                         : __builtin_bit_cast(FragT, *(lds_cu4 *)(kp + (rr * S::NC + 16 * cb) * 64));
                 const floatx4 acc = mfma16x16x32(kf, qf, floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -446,7 +468,8 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
         for (int bq = 0; bq < S::BPC; bq += 2) {
             const int rA = bq / NCB, cbA = bq % NCB;
             const int rB = (bq + 1) / NCB, cbB = (bq + 1) % NCB;
-            const int offA = (rA * S::NC + 16 * cbA) * 64, offB = (rB * S::NC + 16 * cbB) * 64;
+            const int offA = (slot(c0, rA) * S::NC + 16 * cbA) * 64;
+            const int offB = (slot(c0, rB) * S::NC + 16 * cbB) * 64;
             FragT vf[2];
 #pragma unroll
             for (int dh = 0; dh < 2; ++dh) {
@@ -491,9 +514,11 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
                 }
             }
         }
-        kp += RPC * S::NC * 64;
-        vp0 += RPC * S::NC * 64;
-        vp1 += RPC * S::NC * 64;
+        if constexpr (!RING) {
+            kp += RPC * S::NC * 64;
+            vp0 += RPC * S::NC * 64;
+            vp1 += RPC * S::NC * 64;
+        }
         if constexpr (MODE == kClass) {
             bp += RPC * PC;  // the -inf strip is long enough for any chunk
         } else if constexpr (MODE == kInterior) {
@@ -508,7 +533,8 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 
 // One wave's share of a tile: choose its candidate key rows and the bias
 // path, leave o / lsum for store_out.
-template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT = true, bool LSE = false>
+template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT = true, bool LSE = false,
+          int RING = 0>
 __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned char *smem,
                                    const float *btab, int lr, int wave, int lane,
                                    const typename Frag<T>::type &qf, floatx4 (&o)[2], float &lsum,
@@ -520,8 +546,8 @@ __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned 
     const int y1 = t.y0 + QY * wave;
     const int ry = max(t.hy0, min(window_start<WM>(min(y1, H - 1), ks, H), t.hy0 + t.hr - nr));
     if constexpr (S::CLS) {
-        attend<T, QY, QX, NCB, RPC, KS, kClass, WM, CT, LSE>(a, t, smem, btab, lr, wave, ry, lane, qf, o,
-                                                         lsum, st);
+        attend<T, QY, QX, NCB, RPC, KS, kClass, WM, CT, LSE, RING>(a, t, smem, btab, lr, wave, ry, lane,
+                                                               qf, o, lsum, st);
     } else {
         // no query window clamped (SASA windows never are), and the candidate
         // rows / columns start k/2 above / left of the subtile's first query
@@ -530,11 +556,11 @@ __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned 
                                 t.x0 + QX - 1 + r <= W - 1);
         const bool interior = unclamped && ry == y1 - r && t.cx == t.x0 - r;
         if (interior)
-            attend<T, QY, QX, NCB, RPC, KS, kInterior, WM, CT, LSE>(a, t, smem, btab, lr, wave, ry, lane, qf,
-                                                            o, lsum, st);
+            attend<T, QY, QX, NCB, RPC, KS, kInterior, WM, CT, LSE, RING>(a, t, smem, btab, lr, wave, ry,
+                                                                  lane, qf, o, lsum, st);
         else
-            attend<T, QY, QX, NCB, RPC, KS, kGeneral, WM, CT, LSE>(a, t, smem, btab, lr, wave, ry, lane, qf,
-                                                           o, lsum, st);
+            attend<T, QY, QX, NCB, RPC, KS, kGeneral, WM, CT, LSE, RING>(a, t, smem, btab, lr, wave, ry,
+                                                                 lane, qf, o, lsum, st);
     }
 }
 
@@ -787,6 +813,181 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
     }
 }
 
+// Column-run variant for a compile-time kernel size (8 x 8 tiles of 2 x 8
+// subtiles, one 16-column block).  A workgroup walks a run of tiles down one
+// tile column of one map.  Consecutive tiles' halos overlap by all but at
+// most TY rows, so the halo lives in a ring of kRing LDS rows -- map row gy
+// at slot gy & (kRing - 1) -- and each step loads only the rows that enter
+// it (8 of 14 in the interior), into registers while the previous tile is
+// computed.  The first tile of the run is copied HBM -> LDS directly.
+// One run per workgroup; the launch makes the runs as long as it must for
+// all of them to be resident at once.
+constexpr int kRing = 16;
+
+template <int QY, int QX, int NW>
+struct RingRegs {
+    u32x4 k[QY], v[QY];  // QY = TY / NW rows per wave
+    u32x4 q;             // this lane's query fragment
+};
+
+// Issue the loads of the rows [lo, hi) that enter tile t's halo (hi - lo <=
+// TY), wave w taking rows lo + w, lo + w + NW, ...; rows past the range, the
+// map or the tile's columns load as zeros.  Also the tile's query fragment.
+template <int QY, int QX, int NW>
+__device__ inline void load_ring_rows(const Args &a, const Tile &t, int lo, int hi, int wave, int lane,
+                                      RingRegs<QY, QX, NW> &rg)
+{
+    const unsigned map_bytes = (unsigned)a.H * a.W * (kD * 2);
+    const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, t.map_base, kD * 2, map_bytes);
+    const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, t.map_base, kD * 2, map_bytes);
+    const int c_lane = lane >> 2, slot = lane & 3;
+    const int sl = slot ^ ((c_lane >> 2) & 3);
+    const int gx = t.cx + c_lane;
+#pragma unroll
+    for (int j = 0; j < QY; ++j) {
+        const int gy = lo + wave + NW * j;
+        const unsigned off = gy < hi && (unsigned)gy < (unsigned)a.H && (unsigned)gx < (unsigned)a.W
+                                 ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
+                                 : kOutOfRange;
+        rg.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        rg.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    }
+    const int g = lane >> 4, qi = lane & 15;
+    const int y = min(t.y0 + QY * wave + qi / QX, a.H - 1);
+    const int x = min(t.x0 + qi % QX, a.W - 1);
+    const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, t.map_base, kD * 2, map_bytes);
+    rg.q = __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0, 0);
+}
+
+// Write the rows [lo, hi) loaded by load_ring_rows into their ring slots.
+template <int QY, int QX, int NW>
+__device__ inline void write_ring_rows(unsigned char *halo, int lo, int hi, int wave, int lane,
+                                       const RingRegs<QY, QX, NW> &rg)
+{
+#pragma unroll
+    for (int j = 0; j < QY; ++j) {
+        const int gy = lo + wave + NW * j;
+        if (gy < hi) {
+            unsigned char *dk = halo + (unsigned)((gy & (kRing - 1)) * 16) * 64u + 16u * lane;
+            *reinterpret_cast<u32x4 *>(dk) = rg.k[j];
+            *reinterpret_cast<u32x4 *>(dk + halo_bytes(kRing, 16)) = rg.v[j];
+        }
+    }
+}
+
+// Copy tile t's whole halo (rows hy0 .. hy0 + lr - 1, past the map zeros)
+// HBM -> LDS into the ring.
+template <int NW>
+__device__ inline void stage_ring_full(const Args &a, const Tile &t, unsigned char *halo, int lr,
+                                       int wave, int lane)
+{
+    const unsigned map_bytes = (unsigned)a.H * a.W * (kD * 2);
+    const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, t.map_base, kD * 2, map_bytes);
+    const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, t.map_base, kD * 2, map_bytes);
+    const int c_lane = lane >> 2, slot = lane & 3;
+    const int sl = slot ^ ((c_lane >> 2) & 3);
+    const int gx = t.cx + c_lane;
+    for (int r = wave; r < lr; r += NW) {
+        const int gy = t.hy0 + r;
+        const unsigned off = (unsigned)gy < (unsigned)a.H && (unsigned)gx < (unsigned)a.W
+                                 ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
+                                 : kOutOfRange;
+        unsigned char *dk = halo + (unsigned)((gy & (kRing - 1)) * 16) * 64u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)dk, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dk + halo_bytes(kRing, 16)), 16, off,
+                                                 0, 0, 0);
+    }
+}
+
+template <typename T, int KS, int WM, bool LSE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
+na2d_mfma_ring_kernel(Args a)
+{
+    constexpr int QY = 2, QX = 8, NCB = 1, RPC = 8, NW = kWaves;
+    using S = Shape<QY, QX, NCB, RPC, NW, false>;
+    using FragT = typename Frag<T>::type;
+    constexpr int NR = wave_rows(QY, RPC, KS);
+    constexpr int LR = S::TY + KS - 1 > NR ? S::TY + KS - 1 : NR;  // rows a tile's halo needs
+    static_assert(LR < kRing && S::NC == 16, "ring shape");
+    constexpr unsigned BF = bias_floats(false, KS, NR, QY, QX, S::NC, RPC);
+    __shared__ __align__(16) unsigned char halo[2 * kRing * 16 * 64];  // K ring, then V ring
+    __shared__ __align__(16) float btab[BF];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const unsigned run = xcd_tile(blockIdx.x, gridDim.x);
+    if (run >= a.nruns) return;
+    const int col = (int)(run / (unsigned)a.runs_per_col);
+    const int part = (int)run - col * a.runs_per_col;
+    const int ty0 = part * a.run_len, ty1 = min(a.tiles_y, ty0 + a.run_len);
+    if (ty0 >= ty1) return;
+    const int mapi = col / a.tiles_x, tx = col - mapi * a.tiles_x;  // mapi = h * B + b
+    auto tile_at = [&](int ty) {
+        return tile_geometry<S::TY, S::TX, S::NC, WM>(a, (unsigned)((mapi * a.tiles_y + ty) * a.tiles_x + tx));
+    };
+
+    Tile t = tile_at(ty0);
+    {
+        constexpr int NV = raw_per_thread(KS, S::NT);
+        float raw_bias[NV];
+        load_raw_bias<S::NT>(a, KS, t.h, tid, raw_bias);
+        stage_bias<QY, QX, S::NC, RPC, false, S::NT>(a, KS, raw_bias, btab,
+                                                     reinterpret_cast<float *>(halo), NR, tid);
+    }
+    stage_ring_full<NW>(a, t, halo, LR, wave, lane);
+    RingRegs<QY, QX, NW> rg;
+    Tile tn = t;
+    int nlo = 0, nhi = 0;  // rows entering the next tile's halo
+    FragT qf;
+    {
+        const int g = lane >> 4, qi = lane & 15;
+        const int y = min(t.y0 + QY * wave + qi / QX, a.H - 1);
+        const int x = min(t.x0 + qi % QX, a.W - 1);
+        const __amdgpu_buffer_rsrc_t rq =
+            map_rsrc(a.q, t.map_base, kD * 2, (unsigned)a.H * a.W * (kD * 2));
+        qf = __builtin_bit_cast(
+            FragT, __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0, 0));
+    }
+    // loads and stores may retire out of order against each other, so only an
+    // empty counter proves the copies have landed; the next tile's rows are
+    // asked for only then, so that the first halo arrives alone
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (ty0 + 1 < ty1) {
+        tn = tile_at(ty0 + 1);
+        nlo = max(t.hy0 + LR, tn.hy0);
+        nhi = tn.hy0 + LR;
+        load_ring_rows<QY, QX, NW>(a, tn, nlo, nhi, wave, lane, rg);
+    }
+    for (int ty = ty0;;) {
+        floatx4 o[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+        float lsum = 1.f;
+        SoftStats st{0.f, 1.f};
+        if (t.y0 + QY * wave < a.H)  // the bottom tile row may leave whole waves idle
+            attend_wave<T, QY, QX, NCB, RPC, KS, WM, false, LSE, kRing>(a, t, halo, btab, kRing, wave,
+                                                                        lane, qf, o, lsum, st);
+        const Tile done = t;
+        const bool more = ty + 1 < ty1;
+        __syncthreads();  // every wave is done reading the ring
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0);
+            write_ring_rows<QY, QX, NW>(halo, nlo, nhi, wave, lane, rg);
+            qf = __builtin_bit_cast(FragT, rg.q);
+        }
+        store_out<QY, QX, LSE>(a, done, wave, lane, o, lsum, st);
+        if (!more) break;
+        t = tn;
+        ++ty;
+        if (ty + 1 < ty1) {
+            tn = tile_at(ty + 1);
+            nlo = max(t.hy0 + LR, tn.hy0);
+            nhi = tn.hy0 + LR;
+            load_ring_rows<QY, QX, NW>(a, tn, nlo, nhi, wave, lane, rg);
+        }
+        __syncthreads();  // the entering rows are visible
+    }
+}
+
 int device_cus()
 {
     static thread_local int cached_dev = -1, cached_cus = 0;
@@ -881,11 +1082,48 @@ hipError_t launch_pipe(const Problem &p, hipStream_t stream)
                              0, stream);
 }
 
+// The column-run kernel: runs as short as they can be while every run of the
+// launch fits in the resident workgroup slots at once (one run per
+// workgroup), each XCD taking a contiguous stretch of runs.
+// Returns hipErrorNotReady, launching nothing, when the runs would be 2 to 7
+// tiles long: there the persistent register-prefetch kernel measured faster
+// (NAT-Tiny stage 1: 21.9 against 23.3 us; at 448^2, runs of 14 tiles, the
+// ring kernel takes 68 against 73 us, and with one-tile runs 9.4 against
+// 10.2 us at stage 3).
+template <typename T, int KS, int WM, bool LSE>
+hipError_t launch_ring(const Problem &p, hipStream_t stream)
+{
+    using S = Shape<2, 8, 1, 8, kWaves, false>;
+    Args a;
+    if (!make_args<S, 2, 8>(p, a)) return hipErrorInvalidConfiguration;
+    const auto kern = na2d_mfma_ring_kernel<T, KS, WM, LSE>;
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0);
+    if (e != hipSuccess) return e;
+    const int cus = device_cus();
+    if (per_cu <= 0 || cus <= 0) return hipErrorInvalidConfiguration;
+    const uint64_t slots = (uint64_t)cus * per_cu;
+    const uint64_t cols = (uint64_t)p.B * p.heads * a.tiles_x;
+    int len = 1;
+    while (len < a.tiles_y && cols * ((a.tiles_y + len - 1) / len) > slots) ++len;
+    if (len > 1 && len < 8) return hipErrorNotReady;
+    a.run_len = len;
+    a.runs_per_col = (a.tiles_y + len - 1) / len;
+    const uint64_t runs = cols * a.runs_per_col;
+    if (xcd_grid(runs) > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    a.nruns = (unsigned)runs;
+    hipLaunchKernelGGL(kern, dim3((unsigned)xcd_grid(runs)), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <typename T, int WM, bool LSE>
 hipError_t launch_typed(const Problem &p, hipStream_t stream)
 {
     const int ks = p.ksize;
-    if (ks == 7) return launch_pipe<T, 2, 8, 1, 8, 7, 4, WM, LSE, false>(p, stream);
+    if (ks == 7) {
+        const hipError_t e = launch_ring<T, 7, WM, LSE>(p, stream);
+        return e == hipErrorNotReady ? launch_pipe<T, 2, 8, 1, 8, 7, 4, WM, LSE, false>(p, stream) : e;
+    }
     if (ks <= 9) return launch_dma<T, 2, 8, 1, 2, WM, LSE>(p, stream);
     if (ks <= 13) return launch_dma<T, 4, 4, 1, 8, WM, LSE>(p, stream);
     return launch_dma<T, 2, 8, 2, 2, WM, LSE>(p, stream);
