@@ -564,30 +564,87 @@ __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned 
     }
 }
 
-// Normalise and write one wave's 16 outputs: exactly two 16-byte buffer
-// stores per lane, out-of-map queries dropped by the range check.
-// With LSE, lane g == 0 of each query also writes ln(sum of exp(logits)) =
+// Writing one wave's 16 outputs (fp32, 2 KB) takes two steps.
+//
+// stage_out normalises the o fragments and puts them in memory order. The
+// fragments pass through a 1 KB LDS area of the wave's own, in two rounds
+// of 8 queries, and each lane keeps 16 bytes per round. In the fragments a
+// query's 128-byte row is split over four lanes. Staged, one store
+// instruction writes 8 whole rows instead of half of each of 16 rows, which
+// takes the write path far fewer partial lines.
+//
+// Layout: chunk k (16 bytes) of a round's query j sits at chunk
+// 8 j + (k ^ 4 ((j >> 1) & 1)). So the writes (per dh, 32 lanes) reach all
+// 16 bank groups twice, and a read (16 consecutive chunks per 16 lanes)
+// reaches each group once. Lanes of one wave trade data here, so the writes
+// and reads are fenced against code motion.
+//
+// issue_out then issues the stores, non-temporal since nothing reads the
+// output again. Out-of-map queries are dropped by the range check. With LSE,
+// lane g == 0 of each query also writes ln(sum of exp(logits)) =
 // (m + log2 sum) ln 2.
-template <int QY, int QX, bool LSE = false>
-__device__ inline void store_out(const Args &a, const Tile &t, int wave, int lane,
-                                 const floatx4 (&o)[2], float lsum, const SoftStats &st)
+struct OutRegs {
+    floatx4 v[2];  // chunk `lane` of rounds 0 and 1
+    float lse;
+};
+
+__device__ inline int out_chunk(int j, int k) { return 8 * j + (k ^ (4 * ((j >> 1) & 1))); }
+
+template <bool LSE = false>
+__device__ inline void stage_out(int lane, const floatx4 (&o)[2], float lsum, const SoftStats &st,
+                                 float *stage, OutRegs &r)
 {
     const int g = lane >> 4, qi = lane & 15;
     const float inv = __builtin_amdgcn_rcpf(quad_sum(lsum));
-    const int y = t.y0 + QY * wave + qi / QX;
-    const int x = t.x0 + qi % QX;
-    if constexpr (LSE) {
-        const float l = quad_sum(st.l);
-        if (g == 0 && y < a.H && x < a.W)
-            a.lse[t.map_base + (int64_t)y * a.W + x] = (st.m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+    if constexpr (LSE) r.lse = (st.m + __builtin_amdgcn_logf(quad_sum(st.l))) * 0.6931471805599453f;
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+        __builtin_amdgcn_wave_barrier();
+        if ((qi >> 3) == round) {
+#pragma unroll
+            for (int dh = 0; dh < 2; ++dh)
+                *reinterpret_cast<floatx4 *>(stage + 4 * out_chunk(qi & 7, 4 * dh + g)) = o[dh] * inv;
+        }
+        __builtin_amdgcn_wave_barrier();
+        r.v[round] = *reinterpret_cast<const floatx4 *>(stage + 4 * out_chunk(lane >> 3, lane & 7));
     }
-    const unsigned off = y < a.H && x < a.W ? (unsigned)(y * a.W + x) * 128u + 16u * g : kOutOfRange;
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Without an LDS area to spare (the LDS-DMA kernel, whose occupancy its LDS
+// sets), the normalised fragments are stored as they are, with the default
+// cache policy (measured as fast there): v[dh] holds dims 16 dh + 4 g .. + 3
+// of query `lane & 15`.
+template <bool LSE = false>
+__device__ inline void scale_out(const floatx4 (&o)[2], float lsum, const SoftStats &st, OutRegs &r)
+{
+    const float inv = __builtin_amdgcn_rcpf(quad_sum(lsum));
+    if constexpr (LSE) r.lse = (st.m + __builtin_amdgcn_logf(quad_sum(st.l))) * 0.6931471805599453f;
+    r.v[0] = o[0] * inv;
+    r.v[1] = o[1] * inv;
+}
+
+template <int QY, int QX, bool LSE = false, bool STAGED = true>
+__device__ inline void issue_out(const Args &a, const Tile &t, int wave, int lane, const OutRegs &r)
+{
     const __amdgpu_buffer_rsrc_t ro =
         map_rsrc(a.out, t.map_base, kD * 4, (unsigned)a.H * a.W * (kD * 4));
 #pragma unroll
-    for (int dh = 0; dh < 2; ++dh) {
-        const floatx4 v = o[dh] * inv;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off + 64u * dh, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+        // staged: round i, chunk `lane`; else: query lane & 15, dims 16 i + 4 g ..
+        const int q = STAGED ? 8 * i + (lane >> 3) : lane & 15;
+        const unsigned col = STAGED ? 16u * (unsigned)(lane & 7) : 64u * i + 16u * (unsigned)(lane >> 4);
+        const int y = t.y0 + QY * wave + q / QX;
+        const int x = t.x0 + q % QX;
+        const unsigned off = y < a.H && x < a.W ? (unsigned)(y * a.W + x) * 128u + col : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r.v[i]), ro, off, 0,
+                                               STAGED ? kNonTemporal : 0);
+    }
+    if constexpr (LSE) {
+        const int g = lane >> 4, qi = lane & 15;
+        const int y = t.y0 + QY * wave + qi / QX;
+        const int x = t.x0 + qi % QX;
+        if (g == 0 && y < a.H && x < a.W) a.lse[t.map_base + (int64_t)y * a.W + x] = r.lse;
     }
 }
 
@@ -598,8 +655,8 @@ __device__ inline void store_out(const Args &a, const Tile &t, int wave, int lan
 // Persistent workgroups.  Workgroup w takes every G-th tile of its range (the
 // whole tile list, or with xcd_split its XCD's eighth of it, so the
 // workgroups sharing an L2 work on neighbouring tiles).  Per tile: attend,
-// barrier, issue the next tile's copies, store this tile's outputs, wait for
-// the copies only, barrier.
+// barrier, issue the next tile's copies, store this tile's outputs, wait,
+// barrier.
 template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT, bool LSE = false>
 __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
 {
@@ -648,7 +705,9 @@ __global__ __launch_bounds__(kThreads) void na2d_mfma_kernel(Args a)
             }
             stage_tile<T, QY, QX, NCB, RPC>(a, t, smem, lr, wave, lane, qf);
         }
-        store_out<QY, QX, LSE>(a, done, wave, lane, o, lsum, st);
+        OutRegs orr;
+        scale_out<LSE>(o, lsum, st, orr);
+        issue_out<QY, QX, LSE, false>(a, done, wave, lane, orr);
         if (next >= end) break;
         // loads and stores may retire out of order against each other, so
         // only an empty counter proves the copies have landed
@@ -676,7 +735,6 @@ template <typename T, int QY, int QX, int NCB, int RPC, int LR, int NW>
 __device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, int lane,
                                       TileRegs<QY, QX, NCB, LR, NW> &rg, bool live = true)
 {
-    using S = Shape<QY, QX, NCB, RPC, NW>;
     const unsigned map_bytes = (unsigned)a.H * a.W * (kD * 2);
     const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, t.map_base, kD * 2, map_bytes);
     const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, t.map_base, kD * 2, map_bytes);
@@ -703,7 +761,7 @@ __device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, in
     const int x = min(t.x0 + qi % QX, a.W - 1);
     const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, t.map_base, kD * 2, map_bytes);
     rg.q = __builtin_amdgcn_raw_buffer_load_b128(
-        rq, live ? (unsigned)(y * a.W + x) * 64u + 16u * g : kOutOfRange, 0, 0);
+        rq, live ? (unsigned)(y * a.W + x) * 64u + 16u * g : kOutOfRange, 0, kNonTemporal);
 }
 
 // the queries sit after the K and V halos: [wave][lane] 16-byte fragments
@@ -774,6 +832,9 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
     write_tile_regs<QY, QX, NCB, RPC, LR>(halo, wave, lane, rg0);
     __syncthreads();
     const auto *qfrag = reinterpret_cast<const u32x4 *>(halo + q_frag_offset(LR, S::NC)) + tid;
+    // a wave's query fragments (1 KB) are read by that wave alone, at the top
+    // of attend, so the area doubles as the wave's output staging area
+    float *ostage = reinterpret_cast<float *>(halo + q_frag_offset(LR, S::NC)) + 256 * wave;
     while (true) {
         // attend from LDS; the next tile is loading into `rg` meanwhile
         floatx4 o[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
@@ -786,6 +847,8 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
         }
         const Tile done = t;
         const bool more = next < end;
+        OutRegs orr;
+        stage_out<LSE>(lane, o, lsum, st, ostage, orr);
         __syncthreads();  // every wave is done reading the halo (and the bias table)
         if (more) {
             if (tn.h != bias_head) {  // rare: the tile list is head-major
@@ -800,7 +863,7 @@ __global__ __launch_bounds__(64 * NW) void na2d_mfma_pipe_kernel(Args a)
             __builtin_amdgcn_s_waitcnt(0);
             write_tile_regs<QY, QX, NCB, RPC, LR>(halo, wave, lane, rg);
         }
-        store_out<QY, QX, LSE>(a, done, wave, lane, o, lsum, st);
+        issue_out<QY, QX, LSE>(a, done, wave, lane, orr);
         if (!more) break;
         t = tn;
         tile = next;
@@ -856,7 +919,7 @@ __device__ inline void load_ring_rows(const Args &a, const Tile &t, int lo, int 
     const int y = min(t.y0 + QY * wave + qi / QX, a.H - 1);
     const int x = min(t.x0 + qi % QX, a.W - 1);
     const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, t.map_base, kD * 2, map_bytes);
-    rg.q = __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0, 0);
+    rg.q = __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0, kNonTemporal);
 }
 
 // Write the rows [lo, hi) loaded by load_ring_rows into their ring slots.
@@ -912,8 +975,10 @@ na2d_mfma_ring_kernel(Args a)
     constexpr unsigned BF = bias_floats(false, KS, NR, QY, QX, S::NC, RPC);
     __shared__ __align__(16) unsigned char halo[2 * kRing * 16 * 64];  // K ring, then V ring
     __shared__ __align__(16) float btab[BF];
+    __shared__ __align__(16) float ostage_all[NW * 256];  // 1 KB of output staging per wave
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    float *ostage = ostage_all + 256 * wave;
 
     const unsigned run = xcd_tile(blockIdx.x, gridDim.x);
     if (run >= a.nruns) return;
@@ -946,7 +1011,7 @@ na2d_mfma_ring_kernel(Args a)
         const __amdgpu_buffer_rsrc_t rq =
             map_rsrc(a.q, t.map_base, kD * 2, (unsigned)a.H * a.W * (kD * 2));
         qf = __builtin_bit_cast(
-            FragT, __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0, 0));
+            FragT, __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0, kNonTemporal));
     }
     // loads and stores may retire out of order against each other, so only an
     // empty counter proves the copies have landed; the next tile's rows are
@@ -968,13 +1033,15 @@ na2d_mfma_ring_kernel(Args a)
                                                                         lane, qf, o, lsum, st);
         const Tile done = t;
         const bool more = ty + 1 < ty1;
+        OutRegs orr;
+        stage_out<LSE>(lane, o, lsum, st, ostage, orr);
         __syncthreads();  // every wave is done reading the ring
         if (more) {
             __builtin_amdgcn_s_waitcnt(0);
             write_ring_rows<QY, QX, NW>(halo, nlo, nhi, wave, lane, rg);
             qf = __builtin_bit_cast(FragT, rg.q);
         }
-        store_out<QY, QX, LSE>(a, done, wave, lane, o, lsum, st);
+        issue_out<QY, QX, LSE>(a, done, wave, lane, orr);
         if (!more) break;
         t = tn;
         ++ty;

@@ -27,6 +27,9 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 constexpr int kD = 32;        // head dim handled here
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr unsigned kOutOfRange = 0x7ffffff0u;  // byte offset past any map: loads 0, stores dropped
+// Buffer cache policy (gfx950 encoding): bit 1 marks an access non-temporal,
+// for data that is not touched again -- outputs and inputs read exactly once.
+constexpr int kNonTemporal = 2;
 
 template <typename T> struct Frag;
 template <> struct Frag<_Float16> { typedef half8 type; };
