@@ -573,11 +573,11 @@ __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned 
 // instruction writes 8 whole rows instead of half of each of 16 rows, which
 // takes the write path far fewer partial lines.
 //
-// Layout: chunk k (16 bytes) of a round's query j sits at chunk
-// 8 j + (k ^ 4 ((j >> 1) & 1)). So the writes (per dh, 32 lanes) reach all
-// 16 bank groups twice, and a read (16 consecutive chunks per 16 lanes)
-// reaches each group once. Lanes of one wave trade data here, so the writes
-// and reads are fenced against code motion.
+// Layout: chunk k (16 bytes) of a round's query j (0 .. 7) sits at chunk
+// 8 j + (k ^ j). Any 8 consecutive lanes then touch 8 different 16-byte bank
+// groups, both when writing (fixed k, j = 0 .. 7) and when reading (fixed j,
+// k = 0 .. 7). Lanes of one wave trade data here, so the writes and reads
+// are fenced against code motion.
 //
 // issue_out then issues the stores, non-temporal since nothing reads the
 // output again. Out-of-map queries are dropped by the range check. With LSE,
@@ -588,7 +588,7 @@ struct OutRegs {
     float lse;
 };
 
-__device__ inline int out_chunk(int j, int k) { return 8 * j + (k ^ (4 * ((j >> 1) & 1))); }
+__device__ inline int out_chunk(int j, int k) { return 8 * j + (k ^ j); }
 
 template <bool LSE = false>
 __device__ inline void stage_out(int lane, const floatx4 (&o)[2], float lsum, const SoftStats &st,
