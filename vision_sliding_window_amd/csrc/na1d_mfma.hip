@@ -208,7 +208,9 @@ __global__ __launch_bounds__(kT1) void na1d_mfma_kernel(Args1 a)
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh) {
         const floatx4 r = o[dh] * inv;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), ro, off + 64u * dh, 0, 0);
+        // non-temporal: nothing reads the output again
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), ro, off + 64u * dh, 0,
+                                               kNonTemporal);
     }
 }
 

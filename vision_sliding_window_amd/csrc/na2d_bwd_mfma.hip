@@ -226,6 +226,39 @@ __device__ inline void add_bias_grad(const floatx4 &db, float *buf, float *dbias
     }
 }
 
+// Write one fp32 gradient of a wave's 16 positions (2 rows of 8, 32 floats
+// each). In the MFMA fragments, lane (g, c) holds dims 16 dh + 4 g .. + 3 of
+// position c. The values pass through a 1 KB LDS area of the wave, one row
+// of 8 positions per round, so that each store instruction writes 8 whole
+// 128-byte rows instead of half of 16. Chunk k of the round's position j sits
+// at 8 j + (k ^ j), so any 8 consecutive lanes reach 8 different bank groups.
+// Lanes of the wave trade data through the area, hence the code-motion
+// fences. The stores are non-temporal: the gradients are not read again.
+// Every lane of the wave must take part; positions outside the map are not
+// stored.
+__device__ inline void store_rows(float *map, int y0, int x0, int H, int W, const floatx4 (&v)[2],
+                                  float *stage, int lane)
+{
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        __builtin_amdgcn_wave_barrier();
+        if ((c >> 3) == r) {
+            const int j = c & 7;
+#pragma unroll
+            for (int dh = 0; dh < 2; ++dh)
+                *reinterpret_cast<floatx4 *>(stage + 4 * (8 * j + ((4 * dh + g) ^ j))) = v[dh];
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int j = lane >> 3, k = lane & 7;
+        const floatx4 x = *reinterpret_cast<const floatx4 *>(stage + 4 * (8 * j + (k ^ j)));
+        const int y = y0 + r, xx = x0 + j;
+        if (y < H && xx < W)
+            __builtin_nontemporal_store(x, reinterpret_cast<floatx4 *>(map + ((int64_t)y * W + xx) * 32 + 4 * k));
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 // ---------------------------------------------------------------------------
 // Query pass: softmax statistics, g . o, dq and the bias gradient of 16 own
 // queries per wave, from the key blocks that their windows touch.  Writes the
@@ -379,14 +412,11 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
                     dql[dh] = mfma16x16x16(kt, sl, dql[dh], T{});
                 }
             });
-        // lane (g, c): dims 16 dh + 4 g + j of query c
-        if (own_valid) {
-            if (g == 0) a.ws[qi] = make_float2(lse, dd);
-#pragma unroll
-            for (int dh = 0; dh < 2; ++dh)
-                *reinterpret_cast<floatx4 *>(a.dq + qi * 32 + 16 * dh + 4 * g) =
-                    (dq[dh] + dql[dh] * LoScale<T>::down) * a.scale;
-        }
+        if (own_valid && g == 0) a.ws[qi] = make_float2(lse, dd);
+        // the wave's k block area is free once its last block is consumed
+        const floatx4 dqs[2] = {(dq[0] + dql[0] * LoScale<T>::down) * a.scale,
+                                (dq[1] + dql[1] * LoScale<T>::down) * a.scale};
+        store_rows(a.dq + P.base * 32, qy1, P.x0, H, W, dqs, reinterpret_cast<float *>(kbuf[wave]), lane);
     }
     if (a.drpb) {  // the tile's table, summed over tiles by reduce_bias_tables
         __syncthreads();
@@ -556,17 +586,13 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
     };
     // blocks row by row
     pipelined_walk(BlockWalk(ylo, yhi, xlo, nblk), (yhi - ylo + 1) * nblk, load_block, process);
-    // lane (g, c): dims 16 dh + 4 g + j of key c
-    if (own_valid) {
-        const int64_t kj = P.base + (int64_t)ky * W + kx;
-#pragma unroll
-        for (int dh = 0; dh < 2; ++dh) {
-            const floatx4 dkt = dk[dh] + dkl[dh] * LoScale<T>::down;
-            const floatx4 dvt = dv[dh] + dvl[dh] * LoScale<T>::down;
-            *reinterpret_cast<floatx4 *>(a.dk + kj * 32 + 16 * dh + 4 * g) = dkt * a.scale;
-            *reinterpret_cast<floatx4 *>(a.dv + kj * 32 + 16 * dh + 4 * g) = dvt;
-        }
-    }
+    // the wave's q block area is free once its last block is consumed
+    const floatx4 dks[2] = {(dk[0] + dkl[0] * LoScale<T>::down) * a.scale,
+                            (dk[1] + dkl[1] * LoScale<T>::down) * a.scale};
+    const floatx4 dvs[2] = {dv[0] + dvl[0] * LoScale<T>::down, dv[1] + dvl[1] * LoScale<T>::down};
+    float *stage = reinterpret_cast<float *>(qbuf[wave]);
+    store_rows(a.dk + P.base * 32, ky1, P.x0, H, W, dks, stage, lane);
+    store_rows(a.dv + P.base * 32, ky1, P.x0, H, W, dvs, stage, lane);
 }
 
 }  // namespace

@@ -267,7 +267,8 @@ __global__ __launch_bounds__(kT3) void na3d_mfma_kernel(Args3 a)
         if (a.lse && g == 0) a.lse[qi] = (m + __builtin_amdgcn_logf(lq)) * 0.6931471805599453f;
         float *dst = a.out + qi * 32 + 4 * g;
 #pragma unroll
-        for (int dh = 0; dh < 2; ++dh) *reinterpret_cast<floatx4 *>(dst + 16 * dh) = o[dh] * inv;
+        for (int dh = 0; dh < 2; ++dh)  // non-temporal: nothing reads the output again
+            __builtin_nontemporal_store(o[dh] * inv, reinterpret_cast<floatx4 *>(dst + 16 * dh));
     }
 }
 
