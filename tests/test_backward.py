@@ -53,7 +53,9 @@ def check(shape, ks, dtype, with_bias=True, use_lse=False, **kw):
 
 SHAPES = [((1, 2, 13, 17, 32), 3), ((1, 2, 13, 17, 32), 5), ((2, 2, 20, 24, 32), 7),
           ((1, 1, 9, 9, 32), 9), ((1, 1, 7, 30, 32), 7), ((1, 1, 25, 23, 32), 11),
-          ((1, 1, 40, 41, 32), 33), ((1, 1, 6, 6, 32), 1)]
+          ((1, 1, 40, 41, 32), 33), ((1, 1, 6, 6, 32), 1),
+          # the widest windows of the matrix-core passes (k <= 25), ragged tiles on both axes
+          ((1, 1, 27, 29, 32), 13), ((1, 1, 19, 33, 32), 17), ((1, 1, 30, 26, 32), 25)]
 
 
 @pytest.mark.parametrize("shape,ks", SHAPES, ids=str)

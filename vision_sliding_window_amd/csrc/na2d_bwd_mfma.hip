@@ -37,7 +37,6 @@ namespace {
 
 constexpr int kBW = 4;         // waves per workgroup (independent: no barrier in the loops)
 constexpr int kBT = 64 * kBW;  // threads per workgroup
-constexpr int kBMaxRaw = (2 * NA2D_BWD_MFMA_MAX_KSIZE - 1) * (2 * NA2D_BWD_MFMA_MAX_KSIZE - 1);
 
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
@@ -84,12 +83,13 @@ __device__ inline int wstart(int i, int ks, int L)
     return s > L - ks ? L - ks : s;
 }
 
-// Entry i of the LDS bias table, read whether or not the caller will use it
-// (i clamped into the table): the empty asm keeps the read out of a branch
-// on the caller's mask, so the reads of a block issue together.
-__device__ inline float table_at(const float *raw, int i, int n)
+// Entry i (row-major offset from entry (0, 0)) of a padded LDS bias table
+// (stage_padded_bias), read whether or not the caller will use it: the
+// empty asm keeps the read out of a branch on the caller's mask, so the
+// reads of a block issue together.
+__device__ inline float padded_at(const float *t, int i)
 {
-    float b = raw[min(max(i, 0), n - 1)];
+    float b = t[i];
     asm volatile("" : "+v"(b));
     return b;
 }
@@ -135,11 +135,29 @@ __device__ inline Patch patch_of(const BArgs &a, unsigned tile)
 }
 
 // the head's (2k-1)^2 bias table, scaled to log2 units, into LDS
-__device__ inline void stage_raw_bias(const BArgs &a, int h, float *raw)
+// The head's (2k-1)^2 bias table times log2(e)/sqrt(d), in LDS with one
+// zero row above and below and pl / pr zero columns left / right, row stride
+// 2k - 1 + pl + pr. Every entry a pass reads, masked keys included, then lies
+// inside it, so the reads need no clamp: over all windows up to 25 and all
+// map sizes, the query pass reads rows 0 .. 2k-2 and columns -6 .. 2k+14,
+// and the key pass rows -1 .. 2k-1 and columns -22 .. 2k+5. Returns entry
+// (0, 0).
+constexpr int kQPadL = 8, kQPadR = 24, kKvPadL = 24, kKvPadR = 8;
+
+__host__ __device__ constexpr int padded_floats(int ks, int pl, int pr)
 {
-    const int nb = 2 * a.ks - 1;
-    for (int e = threadIdx.x; e < nb * nb; e += kBT)
-        raw[e] = a.rpb ? a.rpb[(int64_t)h * nb * nb + e] * a.c : 0.f;
+    return (2 * ks + 1) * (2 * ks - 1 + pl + pr);
+}
+
+__device__ inline const float *stage_padded_bias(const BArgs &a, int h, float *t, int pl, int pr)
+{
+    const int nb = 2 * a.ks - 1, rs = nb + pl + pr;
+    for (int e = threadIdx.x; e < (nb + 2) * rs; e += kBT) {
+        const int row = e / rs, i = row - 1, j = e - row * rs - pl;
+        const bool in = a.rpb && (unsigned)i < (unsigned)nb && (unsigned)j < (unsigned)nb;
+        t[e] = in ? a.rpb[(int64_t)h * nb * nb + i * nb + j] * a.c : 0.f;
+    }
+    return t + rs + pl;
 }
 
 // slice g of the 16-bit row at (y, x) (lane (g, i) of a block takes x = x0 + i),
@@ -267,15 +285,15 @@ template <typename T>
 __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
 {
     using FragT = typename Frag<T>::type;
-    __shared__ float raw[kBMaxRaw];
-    __shared__ float dbias[kBMaxRaw];                             // the workgroup's bias gradient
     __shared__ __align__(16) unsigned char kbuf[kBW][16 * 64];    // streamed k block [pos][d], 16-bit
     __shared__ __align__(16) float dsbuf[kBW][kDsRows * kDsRow];  // a block's dS by (query, key)
+    extern __shared__ float bias_lds[];  // the padded bias table, then the workgroup's bias gradient
     const unsigned tile = xcd_tile(blockIdx.x, gridDim.x);
     if (tile >= a.ntiles) return;
     const Patch P = patch_of(a, tile);
-    const int H = a.H, W = a.W, ks = a.ks, nb = 2 * ks - 1;
-    stage_raw_bias(a, P.h, raw);
+    const int H = a.H, W = a.W, ks = a.ks, nb = 2 * ks - 1, rs = nb + kQPadL + kQPadR;
+    const float *raw = stage_padded_bias(a, P.h, bias_lds, kQPadL, kQPadR);
+    float *dbias = bias_lds + padded_floats(ks, kQPadL, kQPadR);
     if (a.drpb) {
         for (int e = threadIdx.x; e < nb * nb; e += kBT) dbias[e] = 0.f;
         // the key pass, which runs after this kernel, adds the tables into drpb
@@ -344,14 +362,14 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
                 [&](const u32x4 &kv, int ky, int kxb) {
                     const FragT ka = __builtin_bit_cast(FragT, kv);
                     const bool rowin = own_valid && (unsigned)(ky - sy) < (unsigned)ks;
-                    const int brow = (ky - qy + ks - 1) * nb;
+                    const int brow = (ky - qy + ks - 1) * rs;
                     const floatx4 s = mfma16x16x32(ka, qf, floatx4{0, 0, 0, 0});
                     float t[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int kx = kxb + 4 * g + r;
                         const bool in = rowin && (unsigned)(kx - sx) < (unsigned)ks;
-                        const float b = table_at(raw, brow + kx - qx + ks - 1, nb * nb);
+                        const float b = padded_at(raw, brow + kx - qx + ks - 1);
                         t[r] = in ? s[r] * a.c + b : -INFINITY;
                     }
                     const float mn = fmaxf(fmaxf(m, fmaxf(t[0], t[1])), fmaxf(t[2], t[3]));
@@ -382,7 +400,7 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
             [&](const KV &blk, int ky, int kxb) {
                 const u32x4 kv = blk.k, vv = blk.v;
                 const bool rowin = own_valid && (unsigned)(ky - sy) < (unsigned)ks;
-                const int brow = (ky - qy + ks - 1) * nb;
+                const int brow = (ky - qy + ks - 1) * rs;
                 *reinterpret_cast<u32x4 *>(kb + st_off) = kv;
                 const FragT ka = __builtin_bit_cast(FragT, kv), va = __builtin_bit_cast(FragT, vv);
                 const floatx4 s = mfma16x16x32(ka, qf, floatx4{0, 0, 0, 0});
@@ -395,8 +413,9 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
                 for (int r = 0; r < 4; ++r) {
                     const int kx = kxb + 4 * g + r;
                     const bool in = rowin && (unsigned)(kx - sx) < (unsigned)ks;
-                    const float b = table_at(raw, brow + kx - qx + ks - 1, nb * nb);
-                    const float p = in ? __builtin_amdgcn_exp2f(s[r] * a.c + b - lse) : 0.f;
+                    const float b = padded_at(raw, brow + kx - qx + ks - 1);
+                    const float e = __builtin_amdgcn_exp2f(s[r] * a.c + b - lse);
+                    const float p = in ? e : 0.f;
                     const float ds = p * (gv[r] - dd);
                     db[r] = ds;
                     T h, lo;
@@ -454,24 +473,29 @@ template <typename T>
 __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
 {
     using FragT = typename Frag<T>::type;
-    __shared__ float raw[kBMaxRaw];
     __shared__ __align__(16) unsigned char qbuf[kBW][16 * 64];    // streamed q block [pos][d], 16-bit
     __shared__ __align__(16) unsigned char gbuf[kBW][2][16 * 64]; // streamed g block, hi and lo
+    extern __shared__ float bias_lds[];                           // the padded bias table
     if (a.drpb && blockIdx.x < a.red_jobs) reduce_bias_tables(a, blockIdx.x);
     const unsigned tile = xcd_tile(blockIdx.x, gridDim.x);
     if (tile >= a.ntiles) return;
     const Patch P = patch_of(a, tile);
-    stage_raw_bias(a, P.h, raw);
+    const float *raw = stage_padded_bias(a, P.h, bias_lds, kKvPadL, kKvPadR);
     __syncthreads();
 
     // the wave index is uniform: in a scalar register, loop bounds built on it stay scalar
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int H = a.H, W = a.W, ks = a.ks, nb = 2 * ks - 1;
+    const int H = a.H, W = a.W, ks = a.ks, rs = 2 * ks - 1 + kKvPadL + kKvPadR;
     const int ky1 = P.y0 + 2 * wave;                 // the wave's key rows ky1, ky1 + 1
     if (ky1 >= H) return;
     const int ky = min(ky1 + (c >> 3), H - 1), kx = min(P.x0 + (c & 7), W - 1);
     const bool own_valid = ky1 + (c >> 3) < H && P.x0 + (c & 7) < W;
+    // the queries whose windows hold this lane's key: rows hy0 .. hy1, columns hx0 .. hx1
+    int hy0, hy1, hx0, hx1;
+    holders(ky, ks, H, hy0, hy1);
+    holders(kx, ks, W, hx0, hx1);
+    const unsigned hyn = (unsigned)(hy1 - hy0), hxn = (unsigned)(hx1 - hx0);
     const unsigned map_bytes = (unsigned)H * W * 64u;
     const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, P.base, 64, map_bytes);
     const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, P.base, 64, map_bytes);
@@ -521,7 +545,6 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
     };
     auto process = [&](const Streamed &cur, int y, int xb) {
         {
-            const int sy = wstart(y, ks, H);
             const u32x4 qv = cur.q, g0 = cur.g0, g1 = cur.g1, w01 = cur.w01, w23 = cur.w23;
             // q as A operand (the block's positions as rows), its copy for q^T
             *reinterpret_cast<u32x4 *>(qb + st_off) = qv;
@@ -552,14 +575,16 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
                                  __uint_as_float(w23[1]), __uint_as_float(w23[3])};
             // p and dS for queries (y, xb + 4 g + r) and key c
             v4i16 ph, pl, sh, sl;
-            const bool rowin = own_valid && (unsigned)(ky - sy) < (unsigned)ks;
+            const bool rowin = own_valid && (unsigned)(y - hy0) <= hyn;
+            const int brow = (ky - y + ks - 1) * rs + kx + ks - 1;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int x = xb + 4 * g + r;
-                const bool in = rowin && x < W && (unsigned)(kx - wstart(min(x, W - 1), ks, W)) < (unsigned)ks;
-                // key inside the query's window: the offset indexes the table
-                const float bias = table_at(raw, (ky - y + ks - 1) * nb + (kx - x + ks - 1), nb * nb);
-                const float p = in ? __builtin_amdgcn_exp2f(s[r] * a.c + bias - lse[r]) : 0.f;
+                // the key lies in the window of query (y, x) exactly when the query holds it
+                const bool in = rowin && (unsigned)(x - hx0) <= hxn;
+                const float bias = padded_at(raw, brow - x);
+                const float e = __builtin_amdgcn_exp2f(s[r] * a.c + bias - lse[r]);
+                const float p = in ? e : 0.f;
                 const float ds = p * (gv[r] - dd[r]);
                 T h, l;
                 split<T>(p, h, l);
@@ -632,12 +657,15 @@ hipError_t launch_backward_mfma(const BwdProblem &p, hipStream_t stream)
     a.red_jobs = (unsigned)(((uint64_t)p.B * a.tiles_per_map + kRedRows - 1) / kRedRows * p.heads);
     const dim3 grid((unsigned)xcd_grid(tiles));
     if (a.red_jobs > grid.x) return hipErrorInvalidConfiguration;  // cannot happen: a job spans >= 32 tiles
+    const int nb = 2 * p.ksize - 1;
+    const size_t q_lds = (size_t)(padded_floats(p.ksize, kQPadL, kQPadR) + nb * nb) * 4;
+    const size_t kv_lds = (size_t)padded_floats(p.ksize, kKvPadL, kKvPadR) * 4;
     if (p.dtype == NA2D_F16) {
-        hipLaunchKernelGGL(bwd_q_mfma_kernel<_Float16>, grid, dim3(kBT), 0, stream, a);
-        hipLaunchKernelGGL(bwd_kv_mfma_kernel<_Float16>, grid, dim3(kBT), 0, stream, a);
+        hipLaunchKernelGGL(bwd_q_mfma_kernel<_Float16>, grid, dim3(kBT), q_lds, stream, a);
+        hipLaunchKernelGGL(bwd_kv_mfma_kernel<_Float16>, grid, dim3(kBT), kv_lds, stream, a);
     } else if (p.dtype == NA2D_BF16) {
-        hipLaunchKernelGGL(bwd_q_mfma_kernel<__bf16>, grid, dim3(kBT), 0, stream, a);
-        hipLaunchKernelGGL(bwd_kv_mfma_kernel<__bf16>, grid, dim3(kBT), 0, stream, a);
+        hipLaunchKernelGGL(bwd_q_mfma_kernel<__bf16>, grid, dim3(kBT), q_lds, stream, a);
+        hipLaunchKernelGGL(bwd_kv_mfma_kernel<__bf16>, grid, dim3(kBT), kv_lds, stream, a);
     } else {
         return hipErrorInvalidValue;
     }
