@@ -10,8 +10,9 @@
 //  1. Staging.  The tile's key/value halo -- the union of its queries'
 //     windows, at most TY + ksize - 1 rows by NC = 16 NCB columns -- goes to
 //     LDS as [row][col][d] for both K and V.  The 16-byte d-slice s of pixel
-//     column c sits at slot s ^ ((c >> 2) & 3) so the reads below are free of
-//     bank conflicts.  Pixels outside the map get an out-of-range buffer
+//     column c sits at slot s ^ ((c >> 1) & 3) (halo_slot) so the reads below
+//     are free of bank conflicts: 16-byte reads are served 8 lanes (128
+//     bytes) at a time, 8-byte transposing reads 16 lanes at a time.  Pixels outside the map get an out-of-range buffer
 //     offset and so arrive as zeros.  This is the tiled design of the
 //     paperlayer summary's appendix A.4 (a query tile plus a key tile of side
 //     tq + k - 1 in on-chip memory), re-shaped for 64-lane waves.
@@ -119,6 +120,9 @@ __host__ __device__ constexpr int wave_rows(int QY, int RPC, int ks)
 //  - split layout: the general table [2k][2k], then the interior table
 //    [NR + QY - 1][P].
 __host__ __device__ inline unsigned halo_bytes(int lr, int nc) { return (unsigned)lr * nc * 64u; }
+// LDS slot (16 bytes) of d-slice s of halo column c, and, the XOR being its
+// own inverse, the d-slice held by slot s
+__host__ __device__ constexpr int halo_slot(int s, int c) { return s ^ ((c >> 1) & 3); }
 __host__ __device__ inline unsigned b_offset(int lr, int nc) { return 2u * halo_bytes(lr, nc); }
 __host__ __device__ inline unsigned bi_offset(int lr, int nc, int ks)
 {
@@ -286,7 +290,7 @@ __device__ inline void stage_tile(const Args &a, const Tile &t, unsigned char *s
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             const int c = 16 * cb + c_lane;
-            const int sl = slot ^ ((c >> 2) & 3);  // the d-slice this LDS slot holds
+            const int sl = halo_slot(slot, c);  // the d-slice this LDS slot holds
             const int gx = t.cx + c;
             const unsigned off = (unsigned)gy < (unsigned)a.H && (unsigned)gx < (unsigned)a.W
                                      ? (unsigned)(gy * a.W + gx) * 64u + 16u * sl
@@ -352,14 +356,14 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 
     // K block row: 16 lanes read 16 columns' d-slice g (swizzled slot)
     lds_cu8 *kp = (lds_cu8 *)(smem + (unsigned)(rrel * S::NC) * 64u + (unsigned)qi * 64u +
-                              16u * (unsigned)(g ^ ((qi >> 2) & 3)));
+                              16u * (unsigned)halo_slot(g, qi));
     // V^T fragment via the transposing read: lane (g, qi) supplies dims
     // 16 dh + 4 (qi & 3) .. + 3 of column 4 g + (qi >> 2) and receives dim
     // 16 dh + qi of columns 4 g .. 4 g + 3
     const unsigned char *vbase = smem + halo_bytes(lr, S::NC) + (unsigned)(rrel * S::NC) * 64u +
                                  (unsigned)(4 * g + (qi >> 2)) * 64u + 8u * (unsigned)(qi & 1);
-    lds_cu8 *vp0 = (lds_cu8 *)(vbase + 16u * (unsigned)((0 + ((qi >> 1) & 1)) ^ g));
-    lds_cu8 *vp1 = (lds_cu8 *)(vbase + 16u * (unsigned)((2 + ((qi >> 1) & 1)) ^ g));
+    lds_cu8 *vp0 = (lds_cu8 *)(vbase + 16u * (unsigned)halo_slot(0 + ((qi >> 1) & 1), 4 * g + (qi >> 2)));
+    lds_cu8 *vp1 = (lds_cu8 *)(vbase + 16u * (unsigned)halo_slot(2 + ((qi >> 1) & 1), 4 * g + (qi >> 2)));
 
     lds_cf32 *bp;          // per-lane bias base (advanced per chunk)
     lds_cf32 *bneg = nullptr;
@@ -746,7 +750,7 @@ __device__ inline void load_tile_regs(const Args &a, const Tile &t, int wave, in
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             const int c = 16 * cb + c_lane;
-            const int sl = slot ^ ((c >> 2) & 3);
+            const int sl = halo_slot(slot, c);
             const int gx = t.cx + c;
             const unsigned off =
                 live && r < LR && (unsigned)gy < (unsigned)a.H && (unsigned)gx < (unsigned)a.W
@@ -907,7 +911,7 @@ __device__ inline void load_ring_rows(const Args &a, const Tile &t, int lo, int 
     const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, t.map_base, kD * 2, map_bytes);
     const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, t.map_base, kD * 2, map_bytes);
     const int c_lane = lane >> 2, slot = lane & 3;
-    const int sl = slot ^ ((c_lane >> 2) & 3);
+    const int sl = halo_slot(slot, c_lane);
     const int gx = t.cx + c_lane;
 #pragma unroll
     for (int j = 0; j < QY; ++j) {
@@ -951,7 +955,7 @@ __device__ inline void stage_ring_full(const Args &a, const Tile &t, unsigned ch
     const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, t.map_base, kD * 2, map_bytes);
     const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, t.map_base, kD * 2, map_bytes);
     const int c_lane = lane >> 2, slot = lane & 3;
-    const int sl = slot ^ ((c_lane >> 2) & 3);
+    const int sl = halo_slot(slot, c_lane);
     const int gx = t.cx + c_lane;
     for (int r = wave; r < lr; r += NW) {
         const int gy = t.hy0 + r;
