@@ -89,6 +89,16 @@ struct Args {
     int runs_per_col, run_len;
 };
 
+// Row pitch of a bias table that a wave reads from QY rows at once (its
+// queries' rows): at least `need` floats, and congruent to 32 / QY modulo 32.
+// A b32 LDS read serves 32 lanes per cycle from 32 four-byte banks; with this
+// pitch the QY rows' column ranges fall in disjoint banks instead of two rows
+// meeting in a bank.
+__host__ __device__ constexpr int bias_pitch(int need, int qy)
+{
+    return need + ((32 / qy - need) % 32 + 32) % 32;
+}
+
 template <int QY, int QX, int NCB, int RPC, int NW = kWaves, bool CT = true>
 struct Shape {
     static constexpr int NT = 64 * NW;              // threads per workgroup
@@ -96,7 +106,7 @@ struct Shape {
     static constexpr int TX = QX;                   // tile cols
     static constexpr int NC = 16 * NCB;             // halo cols held in LDS
     static constexpr int BPC = RPC * NCB;           // key blocks per chunk
-    static constexpr int P = NC + QX - 1;           // interior bias table pitch
+    static constexpr int P = bias_pitch(NC + QX - 1, QY);  // interior bias table pitch
     static constexpr int PC = 2 * NC - 1;           // class table pitch
     // class tables (one per column class, see stage_bias) for one 16-column
     // block of 8-query-wide subtiles when CT allows them; otherwise a general
@@ -124,15 +134,11 @@ __host__ __device__ inline unsigned halo_bytes(int lr, int nc) { return (unsigne
 // own inverse, the d-slice held by slot s
 __host__ __device__ constexpr int halo_slot(int s, int c) { return s ^ ((c >> 1) & 3); }
 __host__ __device__ inline unsigned b_offset(int lr, int nc) { return 2u * halo_bytes(lr, nc); }
-__host__ __device__ inline unsigned bi_offset(int lr, int nc, int ks)
-{
-    return b_offset(lr, nc) + (unsigned)(4 * ks * ks) * 4u;
-}
 __host__ __device__ constexpr unsigned class_floats(int ks, int pc) { return (unsigned)ks * (2 * ks - 1) * pc; }
 __host__ __device__ constexpr unsigned bias_floats(bool cls, int ks, int nr, int qy, int qx, int nc, int rpc)
 {
     if (cls) return class_floats(ks, 2 * nc - 1) + (unsigned)(rpc * (2 * nc - 1) + nc);
-    return (unsigned)(4 * ks * ks) + (unsigned)((nr + qy - 1) * (nc + qx - 1));
+    return (unsigned)(2 * ks * bias_pitch(2 * ks, qy)) + (unsigned)((nr + qy - 1) * bias_pitch(nc + qx - 1, qy));
 }
 __host__ __device__ inline unsigned lds_bytes(int lr, int nc, unsigned bfloats)
 {
@@ -186,8 +192,9 @@ __device__ inline Tile tile_geometry(const Args &a, unsigned t)
 //    in [k-1-e_x, 2k-2-e_x], else -inf.  A lane reads element (row i, col c)
 //    of its candidate keys at lane_base + i * PC + c; rows outside its window
 //    read from the -inf strip instead.
-//  - split: the general table [2k][2k] (the (2k-1)^2 table plus a -inf row
-//    and column at index 2k-1) and the interior table [NR + QY - 1][P]: for
+//  - split: the general table [2k][pitch >= 2k] (the (2k-1)^2 table plus
+//    -inf in row 2k-1 and in columns 2k-1 on; see bias_pitch) and the
+//    interior table [NR + QY - 1][P]: for
 //    a subtile none of whose queries is clamped, lane (qy, qx, g) reads
 //    element (row i, col c) at (QY-1-qy+i) * P + (QX-1-qx+c), which holds the
 //    bias of that offset or -inf where |dy| or |dx| exceeds k/2.
@@ -219,8 +226,8 @@ template <int QY, int QX, int NC, int RPC, bool CLS, int NT, int NV>
 __device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV], float *bt,
                                   float *raw, int nr, int tid)
 {
-    constexpr int P = NC + QX - 1, PC = 2 * NC - 1;
-    const int nb = 2 * ks - 1, nraw = nb * nb, tw = 2 * ks, r = ks >> 1;
+    constexpr int P = bias_pitch(NC + QX - 1, QY), PC = 2 * NC - 1;
+    const int nb = 2 * ks - 1, nraw = nb * nb, tw = bias_pitch(2 * ks, QY), r = ks >> 1;
     if (a.rpb) {
 #pragma unroll
         for (int e = 0; e < NV; ++e)
@@ -234,7 +241,7 @@ __device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV],
         n1 = (int)class_floats(ks, PC);
         n = n1 + RPC * PC + NC;
     } else {
-        n1 = tw * tw;
+        n1 = 2 * ks * tw;
         n = n1 + (nr + QY - 1) * P;
     }
     for (int u = tid; u < n; u += NT) {
@@ -345,7 +352,7 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
     const int ks = KS ? KS : a.ks;
     const int H = a.H, W = a.W;
     const int nr = wave_rows(QY, RPC, ks);
-    const int tw = 2 * ks;
+    const int tw = bias_pitch(2 * ks, QY);  // general table pitch
     const int g = lane >> 4, qi = lane & 15;
     const int qy = qi / QX, qx = qi % QX;
     const int y = min(t.y0 + QY * wave + qy, H - 1);
@@ -377,7 +384,7 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
              (S::NC - ks) + 4 * g;
         bneg = (lds_cf32 *)btab + class_floats(ks, PC) + 4 * g;
     } else if constexpr (MODE == kInterior) {
-        bp = (lds_cf32 *)btab + 4 * ks * ks + (QY - 1 - qy) * P + (QX - 1 - qx + 4 * g);
+        bp = (lds_cf32 *)btab + 2 * ks * tw + (QY - 1 - qy) * P + (QX - 1 - qx + 4 * g);
     } else {
         bp = (lds_cf32 *)btab;
         sy = window_start<WM>(y, ks, H);
