@@ -65,12 +65,20 @@ __device__ inline float quad_sum(float v)
 
 // Per-wave LDS copy of a 16-position block [pos][32 dims] of 16-bit values
 // that is read back with ds_read_b64_tr_b16: the 16-byte slice s of position
-// p sits at byte p * 64 + 16 * (s ^ (p & 3)).  The XOR spreads both the
-// stores (lane (g, c) writes slice g of position c) and the transposed reads
-// (four positions per group of 16 lanes) over the banks.
+// p sits at byte p * 64 + 16 * (s ^ copy_swz(p)).
+//
+// 16-byte stores are served 8 lanes (128 bytes) at a time. Lane (g, c)
+// writes slice g of position c, so positions 0, 2, 4, 6 (and 1, 3, 5, 7)
+// need 4 different swizzles. In a transposed read, each group of 16 lanes
+// reads four positions 4 g' .. 4 g' + 3, two slices each. Positions 4 g' and
+// 4 g' + 2 (and likewise + 1 and + 3) need swizzles that differ in bit 1.
+// (p & 2) | ((p >> 2) & 1) meets both conditions. p & 3 met only the second,
+// and conflicted 2-way on the stores.
+__device__ inline unsigned copy_swz(unsigned p) { return (p & 2u) | ((p >> 2) & 1u); }
+
 __device__ inline unsigned stage_off(int g, int c)
 {
-    return (unsigned)c * 64u + 16u * ((unsigned)g ^ ((unsigned)c & 3u));
+    return (unsigned)c * 64u + 16u * ((unsigned)g ^ copy_swz((unsigned)c));
 }
 // Where lane (g, i) reads for the transposed load of dims 16 dh .. 16 dh + 15:
 // dims 16 dh + 4 (i & 3) .. + 3 of position 4 g + (i >> 2); the lane then holds
@@ -79,7 +87,7 @@ __device__ inline unsigned tr_read_off(int g, int i, int dh)
 {
     const unsigned p = 4u * g + ((unsigned)i >> 2);
     const unsigned s = 2u * dh + ((unsigned)(i & 3) >> 1);
-    return p * 64u + 16u * (s ^ (p & 3u)) + 8u * (unsigned)(i & 1);
+    return p * 64u + 16u * (s ^ copy_swz(p)) + 8u * (unsigned)(i & 1);
 }
 
 // Hide a pointer's provenance from the optimiser (an empty asm that "may
