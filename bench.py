@@ -57,9 +57,19 @@ def algorithmic_flops(w) -> int:
 
 
 def source_digest(name: str) -> str:
-    path = os.path.join(ROOT, "vision_sliding_window_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of a kernel source followed by every
+    header it may include (csrc/*.h, then include/*.h, each sorted by name), so
+    that an edit to a shared header also marks a profile as stale."""
+    csrc = os.path.join(ROOT, "vision_sliding_window_amd", "csrc")
+    inc = os.path.join(ROOT, "include")
+    paths = [os.path.join(csrc, name)]
+    paths += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith(".h")]
+    paths += [os.path.join(inc, f) for f in sorted(os.listdir(inc)) if f.endswith(".h")]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str, kid: str):
