@@ -58,11 +58,12 @@ def algorithmic_flops(w) -> int:
 
 def source_digest(name: str) -> str:
     """First 16 hex digits of the SHA-256 of a kernel source followed by every
-    header it may include (csrc/*.h, then include/*.h, each sorted by name), so
-    that an edit to a shared header also marks a profile as stale."""
+    header it may include (csrc/*.h, then include/*.h, each sorted by name) and
+    the build script with its compiler flags, so that an edit to a shared
+    header or a flag also marks a profile as stale."""
     csrc = os.path.join(ROOT, "vision_sliding_window_amd", "csrc")
     inc = os.path.join(ROOT, "include")
-    paths = [os.path.join(csrc, name)]
+    paths = [os.path.join(ROOT, "vision_sliding_window_amd", "_build.py"), os.path.join(csrc, name)]
     paths += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc)) if f.endswith(".h")]
     paths += [os.path.join(inc, f) for f in sorted(os.listdir(inc)) if f.endswith(".h")]
     h = hashlib.sha256()

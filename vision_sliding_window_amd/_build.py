@@ -26,6 +26,12 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function",
          "-I", INCLUDE, "-I", CSRC]
+# Device code only: LLVM's AMDGPU scheduler strategy that groups memory
+# instructions into clauses. Measured against the default on MI355X, same
+# binaries otherwise: stage-1 forward -0.2 to -0.7 us, NA3D -1 us, backward
+# -3 us, k = 13 -1.4 us, outputs bit-identical (only the instruction order
+# changes). The strategy that hoists every load ("max-ilp") was slower.
+HIP_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]
 
 
 def build_library(verbose: bool = False) -> str:
@@ -36,7 +42,7 @@ def build_library(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        lang = ["-x", "hip"] + HIP_FLAGS if src.endswith(".hip") else []
         cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
