@@ -20,12 +20,14 @@
 //     blocks of 16 (one row, 16 consecutive columns).  For a block,
 //     S^T = K_block Q^T is one v_mfma_f32_16x16x32 (d = 32 is the
 //     contraction); each lane then holds one query (lane % 16) and four
-//     consecutive keys (4 (lane / 16) + j).  The scaled bias is added from an
-//     LDS table holding -inf for keys outside the query's window, so the
-//     masked window is exact.
+//     consecutive keys (4 (lane / 16) + j).  The bias comes from an LDS
+//     table holding -inf for keys outside the query's window, so the masked
+//     window is exact; with 8-row chunks it enters as the MFMA's accumulator,
+//     which then returns q.k + B (bias_in_acc).
 //  3. Softmax, single pass over chunks of RPC block rows: the chunk max over
-//     the 4 lanes of a query (v_permlane16/32_swap, no LDS), running max and
-//     sum with rescale, p = exp2(s - m) with log2(e) folded into the scale.
+//     the 4 lanes of a query (v_permlane16/32_swap, no LDS) in log2 units
+//     (c = log2(e)/sqrt(d)); running max and sum with rescale;
+//     p = exp2(c (q.k + B) - m).
 //  4. O^T = V^T P^T, again v_mfma_f32_16x16x32: the S^T layout above is
 //     exactly the B-operand layout of P^T for 32 keys (two blocks), and
 //     ds_read_b64_tr_b16 hands each lane the 4 keys' values of its d from the
@@ -98,6 +100,14 @@ __host__ __device__ constexpr int bias_pitch(int need, int qy)
 {
     return need + ((32 / qy - need) % 32 + 32) % 32;
 }
+
+// With chunks of 8 block rows, every bias read of a chunk issues up front,
+// and the bias enters the QK MFMA as its accumulator (the MFMA returns
+// q.k + B; the logit scale is applied inside the exp's fma): -1 us at k = 7.
+// With short chunks the MFMA would wait on each read; there the tables hold
+// the bias times the scale and it is added by one fma after the MFMA, which
+// measured 0.5 us faster at k = 5 and 9.
+__host__ __device__ constexpr bool bias_in_acc(int rpc) { return rpc >= 8; }
 
 template <int QY, int QX, int NCB, int RPC, int NW = kWaves, bool CT = true>
 struct Shape {
@@ -183,8 +193,9 @@ __device__ inline Tile tile_geometry(const Args &a, unsigned t)
     return g;
 }
 
-// This head's bias tables, times c = log2(e)/sqrt(d), for keys inside a
-// query's window and -inf outside it.  Two layouts:
+// This head's bias tables, for keys inside a query's window and -inf
+// outside it, unscaled or times the logit scale c = log2(e)/sqrt(d) as
+// bias_in_acc says.  Two layouts:
 //  - class (one 16-column block, k <= 9): a query's window columns depend on
 //    e_x = x - sx only (its offset inside the clamped window), so there is one
 //    table per e_x in [0, k): T_e[a][b'] = bias(a, b) for the relative offset
@@ -231,7 +242,7 @@ __device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV],
     if (a.rpb) {
 #pragma unroll
         for (int e = 0; e < NV; ++e)
-            if (e * NT + tid < nraw) raw[e * NT + tid] = val[e] * a.c;
+            if (e * NT + tid < nraw) raw[e * NT + tid] = bias_in_acc(RPC) ? val[e] : val[e] * a.c;
     } else {
         for (int u = tid; u < nraw; u += NT) raw[u] = 0.f;
     }
@@ -349,6 +360,7 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
     using S = Shape<QY, QX, NCB, RPC, kWaves, CT>;
     using FragT = typename Frag<T>::type;
     constexpr int P = S::P, PC = S::PC;
+    constexpr bool kBiasAcc = bias_in_acc(RPC);
     const int ks = KS ? KS : a.ks;
     const int H = a.H, W = a.W;
     const int nr = wave_rows(QY, RPC, ks);
@@ -444,13 +456,19 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
                 const FragT kf =
                     RING ? kring[RING ? rr : 0][cb]
                          : __builtin_bit_cast(FragT, *(lds_cu4 *)(kp + (rr * S::NC + 16 * cb) * 64));
-                const floatx4 acc = mfma16x16x32(kf, qf, floatx4{0.f, 0.f, 0.f, 0.f});
+                // the bias, -inf outside the window (see bias_in_acc)
+                floatx4 bias;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float b;
-                    if constexpr (MODE == kGeneral) b = brow[coloff[cb][j]];
-                    else b = brow[16 * cb + j];
-                    sc[rr][cb][j] = fmaf(acc[j], a.c, b);
+                for (int j = 0; j < 4; ++j)
+                    bias[j] = MODE == kGeneral ? brow[coloff[cb][j]] : brow[16 * cb + j];
+                if constexpr (kBiasAcc) {
+                    const floatx4 acc = mfma16x16x32(kf, qf, bias);  // q.k + B
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sc[rr][cb][j] = acc[j];
+                } else {
+                    const floatx4 acc = mfma16x16x32(kf, qf, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sc[rr][cb][j] = fmaf(acc[j], a.c, bias[j]);  // log2 units
                 }
             }
         }
@@ -461,7 +479,9 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) mc = fmaxf(mc, sc[rr][cb][j]);
-        mc = quad_max(mc);
+        // in log2 units; with the bias in the accumulator the scores are not
+        // yet scaled, and c > 0 makes this the max of the scaled ones, bit for bit
+        mc = kBiasAcc ? quad_max(mc) * a.c : quad_max(mc);
         const float mnew = fmaxf(m, mc);
         const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
         if (c0 > 0) {  // rescale what earlier chunks accumulated
@@ -492,9 +512,10 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
             }
             float p[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                p[j] = __builtin_amdgcn_exp2f(sc[rA][cbA][j] - muse);
-                p[4 + j] = __builtin_amdgcn_exp2f(sc[rB][cbB][j] - muse);
+            for (int j = 0; j < 4; ++j) {  // exp2(c (q.k + B) - m)
+                p[j] = __builtin_amdgcn_exp2f(kBiasAcc ? fmaf(sc[rA][cbA][j], a.c, -muse) : sc[rA][cbA][j] - muse);
+                p[4 + j] =
+                    __builtin_amdgcn_exp2f(kBiasAcc ? fmaf(sc[rB][cbB][j], a.c, -muse) : sc[rB][cbB][j] - muse);
             }
             if constexpr (__is_same(T, _Float16)) {
                 half8 pf;
