@@ -680,10 +680,6 @@ __device__ inline void issue_out(const Args &a, const Tile &t, int wave, int lan
     }
 }
 
-// s_waitcnt on vmcnt alone (gfx9 encoding: expcnt and lgkmcnt left at their maxima).
-#define NA2D_WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
 // Persistent workgroups.  Workgroup w takes every G-th tile of its range (the
 // whole tile list, or with xcd_split its XCD's eighth of it, so the
 // workgroups sharing an L2 work on neighbouring tiles).  Per tile: attend,
