@@ -35,14 +35,16 @@
 //     is split into bf16 hi + lo parts (two products), so the weights keep
 //     ~16 bits either way.
 //  5. out = O / sum in fp32 with 16-byte buffer stores (out-of-map lanes get
-//     an out-of-range offset and are dropped).
-// Two kernels share steps 2-5.  na2d_mfma_kernel (any kernel size) copies the
-// halo HBM -> LDS with buffer_load ... lds (no VGPRs) and then waits for it;
-// na2d_mfma_pipe_kernel (a compile-time kernel size) loads the next tile's
-// halo into registers while the current tile is computed, and writes it to
-// LDS between two barriers.  Either way each iteration drains the vector
-// memory counter completely: loads and stores may retire out of order against
-// each other, so a partial count would not prove the halo had landed.
+//     an out-of-range offset and are dropped).  The k = 7 kernels first pass
+//     a wave's outputs through LDS, so that each store writes whole rows.
+// Three kernels share steps 2-5.  na2d_mfma_kernel (any kernel size) copies
+// the halo HBM -> LDS with buffer_load ... lds (no VGPRs) and then waits for
+// it; na2d_mfma_pipe_kernel (a compile-time kernel size) loads the next
+// tile's halo into registers while the current tile is computed, and writes
+// it to LDS between two barriers; na2d_mfma_ring_kernel walks a column of
+// tiles and loads only the halo rows that enter.  Each iteration drains the
+// vector memory counter completely: loads and stores may retire out of order
+// against each other, so a partial count would not prove the halo had landed.
 // No ksize^2-wide tensor ever leaves the chip.
 #include "na2d.h"
 #include "na2d_launch.h"
@@ -564,7 +566,7 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
 }
 
 // One wave's share of a tile: choose its candidate key rows and the bias
-// path, leave o / lsum for store_out.
+// path, leave o / lsum for stage_out (or scale_out).
 template <typename T, int QY, int QX, int NCB, int RPC, int KS, int WM, bool CT = true, bool LSE = false,
           int RING = 0>
 __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned char *smem,
