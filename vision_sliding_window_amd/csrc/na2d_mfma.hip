@@ -139,8 +139,8 @@ __host__ __device__ constexpr int wave_rows(int QY, int RPC, int ks)
 // the head's bias tables (see stage_bias):
 //  - class layout: k tables [2k-1][PC] floats, then a -inf strip of
 //    RPC * PC + NC floats;
-//  - split layout: the general table [2k][2k], then the interior table
-//    [NR + QY - 1][P].
+//  - split layout: the general table [2k + 1][2k] (a -inf row, then the
+//    general rows), then the interior table [NR + QY - 1][P].
 __host__ __device__ inline unsigned halo_bytes(int lr, int nc) { return (unsigned)lr * nc * 64u; }
 // LDS slot (16 bytes) of d-slice s of halo column c, and, the XOR being its
 // own inverse, the d-slice held by slot s
@@ -150,7 +150,8 @@ __host__ __device__ constexpr unsigned class_floats(int ks, int pc) { return (un
 __host__ __device__ constexpr unsigned bias_floats(bool cls, int ks, int nr, int qy, int qx, int nc, int rpc)
 {
     if (cls) return class_floats(ks, 2 * nc - 1) + (unsigned)(rpc * (2 * nc - 1) + nc);
-    return (unsigned)(2 * ks * bias_pitch(2 * ks, qy)) + (unsigned)((nr + qy - 1) * bias_pitch(nc + qx - 1, qy));
+    return (unsigned)((2 * ks + 1) * bias_pitch(2 * ks, qy)) +
+           (unsigned)((nr + qy - 1) * bias_pitch(nc + qx - 1, qy));
 }
 __host__ __device__ inline unsigned lds_bytes(int lr, int nc, unsigned bfloats)
 {
@@ -205,8 +206,10 @@ __device__ inline Tile tile_geometry(const Args &a, unsigned t)
 //    in [k-1-e_x, 2k-2-e_x], else -inf.  A lane reads element (row i, col c)
 //    of its candidate keys at lane_base + i * PC + c; rows outside its window
 //    read from the -inf strip instead.
-//  - split: the general table [2k][pitch >= 2k] (the (2k-1)^2 table plus
-//    -inf in row 2k-1 and in columns 2k-1 on; see bias_pitch) and the
+//  - split: the general table [2k + 1][pitch >= 2k]: a -inf row, the
+//    (2k-1)^2 table, then a -inf row, with -inf in columns 2k-1 on (see
+//    bias_pitch). Row a + 1 holds row offset a, so that a candidate row one
+//    above a window (relative offset -k) still reads inside the table. Then the
 //    interior table [NR + QY - 1][P]: for
 //    a subtile none of whose queries is clamped, lane (qy, qx, g) reads
 //    element (row i, col c) at (QY-1-qy+i) * P + (QX-1-qx+c), which holds the
@@ -254,7 +257,7 @@ __device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV],
         n1 = (int)class_floats(ks, PC);
         n = n1 + RPC * PC + NC;
     } else {
-        n1 = 2 * ks * tw;
+        n1 = (2 * ks + 1) * tw;
         n = n1 + (nr + QY - 1) * P;
     }
     for (int u = tid; u < n; u += NT) {
@@ -270,6 +273,7 @@ __device__ inline void stage_bias(const Args &a, int ks, const float (&val)[NV],
             if (u < n1) {
                 br = u / tw;
                 bc = u - br * tw;
+                --br;  // row 0 is the -inf row above the table
                 if (br >= nb || bc >= nb) br = -1;
             } else {
                 const int ui = u - n1, ai = ui / P, bi = ui - ai * P;
@@ -389,6 +393,14 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
     lds_cf32 *bp;          // per-lane bias base (advanced per chunk)
     lds_cf32 *bneg = nullptr;
     int sy = 0, lo = 0, coloff[NCB][4];
+    // General path with a compile-time kernel size and one chunk: the table
+    // pitch is a constant, so each of a lane's columns keeps one pointer and
+    // a row is an instruction offset from it. Rows [nr - k, k) lie inside
+    // every window; the others (the first and last for QY = 2) are masked by
+    // a select on the value read.
+    constexpr bool kFixedGeneral = MODE == kGeneral && KS && RPC == wave_rows(QY, RPC, KS);
+    constexpr int kTW = KS ? bias_pitch(2 * KS, QY) : 0;
+    lds_cf32 *gp[kFixedGeneral ? NCB : 1][4];
     if constexpr (MODE == kClass) {
         sy = window_start<WM>(y, ks, H);
         const int ex = x - window_start<WM>(x, ks, W);
@@ -398,9 +410,9 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
              (S::NC - ks) + 4 * g;
         bneg = (lds_cf32 *)btab + class_floats(ks, PC) + 4 * g;
     } else if constexpr (MODE == kInterior) {
-        bp = (lds_cf32 *)btab + 2 * ks * tw + (QY - 1 - qy) * P + (QX - 1 - qx + 4 * g);
+        bp = (lds_cf32 *)btab + (2 * ks + 1) * tw + (QY - 1 - qy) * P + (QX - 1 - qx + 4 * g);
     } else {
-        bp = (lds_cf32 *)btab;
+        bp = (lds_cf32 *)btab + tw;  // row offset 0 (past the -inf row)
         sy = window_start<WM>(y, ks, H);
         const int sx = window_start<WM>(x, ks, W);
 #pragma unroll
@@ -410,6 +422,19 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
                 const int col = t.cx + 16 * cb + 4 * g + j;
                 coloff[cb][j] = (unsigned)(col - sx) < (unsigned)ks ? col - x + ks - 1 : 2 * ks - 1;
             }
+        if constexpr (kFixedGeneral) {
+            // candidate row r reads table row (ry + r - y + k - 1) + 1, which
+            // lies in [0, 2k] for every NA map, so one pointer per column
+            // serves all rows
+            lo = sy - ry;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    gp[cb][j] = (lds_cf32 *)btab + (ry - y + ks) * kTW + coloff[cb][j];
+                    opaque(gp[cb][j]);
+                }
+        }
     }
     // keep each per-lane LDS pointer in one register, so that every access
     // below is that register plus an instruction offset
@@ -440,7 +465,7 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
         }
 #pragma unroll
         for (int rr = 0; rr < RPC; ++rr) {
-            lds_cf32 *brow;
+            lds_cf32 *brow = bp;
             if constexpr (MODE == kClass) {
                 // rows k .. nr-1-(nr-k) are inside every window when nr is fixed
                 const bool always = KS && RPC == wave_rows(QY, RPC, KS) &&
@@ -448,7 +473,7 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
                 brow = (always || (unsigned)(c0 + rr - lo) < (unsigned)ks ? bp : bneg) + rr * PC;
             } else if constexpr (MODE == kInterior) {
                 brow = bp + rr * P;
-            } else {
+            } else if constexpr (!kFixedGeneral) {
                 const int krow = ry + c0 + rr;
                 brow = bp + ((unsigned)(krow - sy) < (unsigned)ks ? (krow - y + ks - 1) * tw
                                                                    : (2 * ks - 1) * tw);
@@ -460,9 +485,20 @@ __device__ inline void attend(const Args &a, const Tile &t, const unsigned char 
                          : __builtin_bit_cast(FragT, *(lds_cu4 *)(kp + (rr * S::NC + 16 * cb) * 64));
                 // the bias, -inf outside the window (see bias_in_acc)
                 floatx4 bias;
+                if constexpr (kFixedGeneral) {
+                    constexpr int nr1 = wave_rows(QY, RPC, KS);
+                    const bool always = rr >= nr1 - KS && rr < KS;
+                    const bool rowin = always || (unsigned)(rr - lo) < (unsigned)KS;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    bias[j] = MODE == kGeneral ? brow[coloff[cb][j]] : brow[16 * cb + j];
+                    for (int j = 0; j < 4; ++j) {
+                        bias[j] = gp[cb][j][rr * kTW];
+                        if (!always) bias[j] = rowin ? bias[j] : -__builtin_inff();
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        bias[j] = MODE == kGeneral ? brow[coloff[cb][j]] : brow[16 * cb + j];
+                }
                 if constexpr (kBiasAcc) {
                     const floatx4 acc = mfma16x16x32(kf, qf, bias);  // q.k + B
 #pragma unroll
