@@ -41,7 +41,10 @@ def test_na1d(shape, ks, dtype):
 
 
 NA3D = [((1, 2, 6, 7, 9, 32), 3), ((2, 1, 5, 5, 5, 32), 5), ((1, 2, 7, 9, 11, 32), 5),
-        ((1, 1, 4, 12, 10, 16), 3), ((1, 1, 9, 9, 9, 64), 7)]
+        ((1, 1, 4, 12, 10, 16), 3), ((1, 1, 9, 9, 9, 64), 7),
+        # volumes with waves none of whose windows is clamped (the matrix-core
+        # kernel's interior path), next to border waves, for each block shape
+        ((1, 2, 6, 16, 16, 32), 3), ((1, 1, 9, 20, 20, 32), 5), ((1, 1, 9, 16, 24, 32), 7)]
 
 
 @pytest.mark.parametrize("shape,ks", NA3D, ids=str)
