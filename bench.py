@@ -311,6 +311,8 @@ def main():
     ap.add_argument("--algo", default="auto", choices=sorted(ALGOS))
     ap.add_argument("--min-footprint-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-floor", action="store_true",
+                    help="skip the streaming reference leg (16-bit workloads)")
     ap.add_argument("--no-hot", action="store_true",
                     help="skip the cache-resident (single-set) timing")
     ap.add_argument("--q-scale", type=float, default=1.0,
@@ -417,6 +419,31 @@ def main():
         torch.cuda.synchronize()
         hot_ms = hs.elapsed_time(he) / args.steps
 
+    # labelled reference leg: a plain streaming kernel that reads the same
+    # three 16-bit inputs and writes the same fp32 output, once each, over the
+    # same rotating sets -- the rate a launch of these bytes gets with no
+    # attention work (not part of the step)
+    floor_ms = None
+    if w.dtype != "f32" and not args.no_stream_floor:
+        elems = w.queries * w.d
+
+        def stream_ref(i):
+            q, k, v, out = sets[i % nsets]
+            st = lib.na_stream_reference(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         elems, sptr)
+            if st != 0:
+                raise RuntimeError("stream reference failed: %s" % na2d.na2d_strerror(st))
+
+        for i in range(args.warmup):
+            stream_ref(i)
+        fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fs.record(stream)
+        for i in range(args.steps):
+            stream_ref(i)
+        fe.record(stream)
+        torch.cuda.synchronize()
+        floor_ms = fs.elapsed_time(fe) / args.steps
+
     copy_gbs = d2d_copy_gbs(torch, dev)
     value = w.queries / (ms * 1e-3)
     gbs = set_bytes / (ms * 1e-3) / 1e9
@@ -446,6 +473,10 @@ def main():
                    "clock_settle_ms": args.settle_ms, "clock_settle_launches": settled,
                    "footprint_bytes": nsets * set_bytes, "algorithmic_bytes_per_step": set_bytes,
                    "hot_ms_per_step": None if hot_ms is None else round(hot_ms, 6),
+                   "stream_floor_us": None if floor_ms is None else round(floor_ms * 1e3, 3),
+                   "stream_floor_note": "na_stream_reference over the same rotating sets: "
+                                        "the same bytes read and written once, no attention",
+                   "frac_of_stream_floor": None if floor_ms is None else round(floor_ms / ms, 4),
                    "useful_tflops": round(tflops, 2),
                    "d2d_copy_gbs": round(copy_gbs, 1),
                    "frac_of_d2d_copy": round(gbs / copy_gbs, 4),

@@ -29,8 +29,9 @@
  *    means no positional bias.
  *  - All pointers must be 16-byte aligned; out must not overlap q, k, v or rpb.
  *  - The caller owns every buffer.  The library allocates nothing, frees
- *    nothing and never synchronises; it keeps no state, so concurrent calls
- *    from several threads are safe.
+ *    nothing and never synchronises.  Its only state is a process-wide,
+ *    mutex-guarded cache of each kernel's occupancy per device (queried on
+ *    first use), so concurrent calls from several threads are safe.
  *  - The call is asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream).  Arguments are checked on the host before anything is
  *    launched: an invalid call returns a negative status and launches
@@ -216,6 +217,12 @@ int na2d_backward(const void *q, const void *k, const void *v, const float *rpb,
                   float *dv, float *drpb, void *workspace, int B, int heads, int H, int W, int d,
                   int ksize, int dtype, void *stream);
 
+/* The kernels na2d_backward runs for these sizes (NA2D_ALGO_MFMA: both
+ * passes on the matrix cores, for 16-bit inputs, d = 32, ksize <=
+ * NA2D_BWD_MFMA_MAX_KSIZE and H * W * 128 < 2^31; NA2D_ALGO_VALU otherwise),
+ * or a negative status if the sizes are invalid.  Host only. */
+int na2d_backward_select_algo(int H, int W, int d, int ksize, int dtype);
+
 /* Bytes of workspace na2d_backward needs for these sizes and window (0 if
  * they are invalid). */
 long long na2d_backward_workspace_bytes(int B, int heads, int H, int W, int ksize);
@@ -227,6 +234,17 @@ int na2d_backward_check_args(const void *q, const void *k, const void *v, const 
                              const float *drpb, const void *workspace, int B, int heads, int H,
                              int W, int d, int ksize, int dtype);
 
+/* A memory-rate reference, not part of the attention: reads `elems` fp16
+ * values from each of a, b and c and writes out[i] = a[i] + b[i] + c[i] in
+ * float32 -- the bytes a fused forward with 16-bit inputs moves for `elems`
+ * input elements per tensor, read and written once each, with no attention
+ * work.  Pointers are device memory, 16-byte aligned; elems > 0 and a
+ * multiple of 8.  Asynchronous on `stream`.  Returns NA2D_OK, or
+ * NA2D_ERR_NULL / NA2D_ERR_SHAPE / NA2D_ERR_ALIGN before launching, or
+ * NA2D_ERR_HIP. */
+int na_stream_reference(const void *a, const void *b, const void *c, float *out, long long elems,
+                        void *stream);
+
 /* Static text for a status code. */
 const char *na2d_strerror(int status);
 
@@ -235,6 +253,11 @@ const char *na2d_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int na2d_version(void);
+
+/* Diagnostic: occupancy queries the library has made in this process.  Each
+ * kernel is queried once per device and LDS size, on its first launch; a
+ * repeated call with the same sizes adds none. */
+long long na2d_occupancy_queries(void);
 
 #ifdef __cplusplus
 }

@@ -277,5 +277,26 @@ def pin_lse(orc):
         assert np.array_equal(out, orc.na2d_forward(q, k, vv, rpb, n))
 
 
+def pin_sampled_index(orc):
+    """The sampled form returns, for each linear query index
+    ((b * heads + h) * H + y) * W + x, exactly the row of the whole-map forward
+    (already pinned above) at that index: on ragged maps with several batches
+    and heads, where a swapped batch/head or row/column split lands on another
+    query. Indices come in shuffled order, with the first and last query."""
+    r = _rng(20)
+    for (B, heads, H, W, d, ks) in [(3, 2, 9, 11, 8, 5), (2, 3, 7, 12, 4, 7), (4, 5, 6, 5, 8, 3)]:
+        q = r.standard_normal((B, heads, H, W, d))
+        k = r.standard_normal((B, heads, H, W, d))
+        v = r.standard_normal((B, heads, H, W, d))
+        rpb = r.standard_normal((heads, 2 * ks - 1, 2 * ks - 1))
+        full = orc.na2d_forward(q, k, v, rpb, ks).reshape(-1, d)
+        n = full.shape[0]
+        idx = np.concatenate([[n - 1, 0], r.permutation(n)[: n // 2]]).astype(np.int64)
+        got = orc.na2d_forward_sampled(q, k, v, rpb, ks, idx)
+        assert got.shape == (idx.size, d)
+        assert np.array_equal(got, full[idx]), (B, heads, H, W, ks)
+
+
 ALL_PINS = [pin_span, pin_self_attention, pin_sdpa, pin_translation, pin_flip_transpose,
-            pin_box_mean, pin_identity, pin_bias_offset, pin_softmax_shift, pin_lse]
+            pin_box_mean, pin_identity, pin_bias_offset, pin_softmax_shift, pin_lse,
+            pin_sampled_index]

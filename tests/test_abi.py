@@ -283,3 +283,41 @@ def test_holder_ranges_closed_form():
                 lo = 0 if j < k else j - k // 2
                 hi = L - 1 if j >= L - k else j + k // 2
                 assert members == list(range(lo, hi + 1)), (k, L, j)
+
+
+def test_backward_select_algo():
+    """The matrix-core backward takes 16-bit inputs, d = 32, k <= 25 and maps
+    whose fp32 rows fit 32-bit byte offsets (H * W * 128 < 2^31); past that
+    bound, and for anything else, the VALU kernels (64-bit offsets) run."""
+    MFMA, VALU = na2d.NA2D_ALGO_MFMA, na2d.NA2D_ALGO_VALU
+    sel = na2d.na2d_backward_select_algo
+    assert sel(56, 56, 32, 7, na2d.NA2D_F16) == MFMA
+    assert sel(56, 56, 32, 7, na2d.NA2D_BF16) == MFMA
+    assert sel(56, 56, 32, 7, na2d.NA2D_F32) == VALU
+    assert sel(56, 56, 64, 7, na2d.NA2D_F16) == VALU
+    assert sel(128, 128, 32, 25, na2d.NA2D_F16) == MFMA
+    assert sel(128, 128, 32, 27, na2d.NA2D_F16) == VALU
+    # the largest map the matrix-core passes address, and the first past it
+    assert 4096 * 4095 * 128 < 2 ** 31 <= 4096 * 4096 * 128
+    assert sel(4096, 4095, 32, 7, na2d.NA2D_F16) == MFMA
+    assert sel(4096, 4096, 32, 7, na2d.NA2D_F16) == VALU
+    assert sel(16384, 1024, 32, 7, na2d.NA2D_BF16) == VALU
+    assert sel(56, 56, 32, 8, na2d.NA2D_F16) == na2d.NA2D_ERR_KSIZE
+    assert sel(56, 56, 48, 7, na2d.NA2D_F16) == na2d.NA2D_ERR_UNSUPPORTED
+    assert sel(56, 56, 32, 7, 9) == na2d.NA2D_ERR_DTYPE
+
+
+def test_occupancy_queries_start_at_zero():
+    """No kernel has been launched on this CPU-only process, so the library
+    has made no occupancy query."""
+    assert na2d.na2d_occupancy_queries() == 0
+
+
+def test_stream_reference_rejects_before_launch():
+    ref = na2d.na_stream_reference
+    assert ref(None, K, V, OUT, 64) == na2d.NA2D_ERR_NULL
+    assert ref(Q, K, V, None, 64) == na2d.NA2D_ERR_NULL
+    assert ref(Q, K, V, OUT, 0) == na2d.NA2D_ERR_SHAPE
+    assert ref(Q, K, V, OUT, 60) == na2d.NA2D_ERR_SHAPE    # not a multiple of 8
+    assert ref(Q + 8, K, V, OUT, 64) == na2d.NA2D_ERR_ALIGN
+    assert ref(Q, K, V, OUT + 4, 64) == na2d.NA2D_ERR_ALIGN

@@ -110,13 +110,10 @@ def test_forward_past_2_31_elements(ks):
     torch.cuda.empty_cache()
 
 
-def test_backward_past_2_31_elements():
-    B, heads, H, W, d, ks = 80, 16, 256, 256, 32, 7
-    assert B * heads * H * W * d > 2 ** 31
-    print("backward past 2^31 elements", flush=True)
-    q, k, v = (draw((B, heads, H, W, d), torch.float16, s) for s in (21, 22, 23))
-    rpb = draw((heads, 2 * ks - 1, 2 * ks - 1), torch.float32, 24)
-    g = draw((B, heads, H, W, d), torch.float32, 25)
+def check_backward(B, heads, H, W, d, ks, seed, n_sampled):
+    q, k, v = (draw((B, heads, H, W, d), torch.float16, s) for s in (seed, seed + 1, seed + 2))
+    rpb = draw((heads, 2 * ks - 1, 2 * ks - 1), torch.float32, seed + 3)
+    g = draw((B, heads, H, W, d), torch.float32, seed + 4)
     out = na2d.forward(q, k, v, rpb, ks, algo=na2d.NA2D_ALGO_VALU)  # fp32 arithmetic
     lse = na2d.forward_lse(q, k, v, rpb, ks)[1]
     dq, dk, dv, drpb = na2d.backward(q, k, v, rpb, out, g, ks, lse=lse)
@@ -134,7 +131,7 @@ def test_backward_past_2_31_elements():
     assert (dbsum.abs() <= 1e-5 * drpb.abs().sum(dim=(1, 2), dtype=f64) + 1e-3).all(), dbsum
     # dq of sampled queries against the oracle's gradients on their crops
     worst = 0.0
-    for m, y, x in sample_queries(B, heads, H, W, 32, 26):
+    for m, y, x in sample_queries(B, heads, H, W, n_sampled, seed + 5):
         ys, xs = crop_span(y, H, ks), crop_span(x, W, ks)
         hh = m % heads
         want = oracle.na2d_backward(crop(q, m, ys, xs, heads), crop(k, m, ys, xs, heads),
@@ -148,3 +145,22 @@ def test_backward_past_2_31_elements():
     assert worst <= 1e-4
     del q, k, v, g, out, lse, dq, dk, dv, drpb
     torch.cuda.empty_cache()
+
+
+def test_backward_past_2_31_elements():
+    B, heads, H, W, d, ks = 80, 16, 256, 256, 32, 7
+    assert B * heads * H * W * d > 2 ** 31
+    print("backward past 2^31 elements", flush=True)
+    check_backward(B, heads, H, W, d, ks, 21, 32)
+
+
+@pytest.mark.parametrize("H,W,algo", [(4096, 4095, na2d.NA2D_ALGO_MFMA),
+                                      (4096, 4096, na2d.NA2D_ALGO_VALU)])
+def test_backward_largest_map(H, W, algo):
+    """The largest map whose fp32 rows the matrix-core backward addresses with
+    32-bit byte offsets (H * W * 128 < 2^31), and the first map past it, which
+    the selection sends to the VALU kernels (64-bit offsets)."""
+    d, ks = 32, 7
+    assert na2d.na2d_backward_select_algo(H, W, d, ks, na2d.NA2D_F16) == algo
+    print("backward largest map", H, W, "algo", algo, flush=True)
+    check_backward(1, 1, H, W, d, ks, 31, 24)

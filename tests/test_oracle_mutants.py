@@ -28,6 +28,15 @@ MUTANTS = {
                         "const double *kj = q + (map + (int64_t)ky * W + kx) * d;"),
     "lse_without_max": ("if (lse) *lse = m + log(z);", "if (lse) *lse = log(z);"),
     "lse_log2": ("if (lse) *lse = m + log(z);", "if (lse) *lse = m + log2(z);"),
+    # the sampled form's split of a linear query index
+    "sampled_batch_head_swapped": (
+        "const int h = (int)((p / ((int64_t)W * H)) % heads);\n"
+        "            const int64_t b = p / ((int64_t)W * H * heads);",
+        "const int h = (int)(p / ((int64_t)W * H * B));\n"
+        "            const int64_t b = (p / ((int64_t)W * H)) % B;"),
+    "sampled_row_col_swapped": (
+        "const int x = (int)(p % W);\n            const int y = (int)((p / W) % H);",
+        "const int y = (int)(p % H);\n            const int x = (int)((p / H) % W);"),
 }
 
 

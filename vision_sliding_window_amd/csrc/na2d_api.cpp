@@ -265,6 +265,16 @@ extern "C" int sasa2d_forward(const void *q, const void *k, const void *v, const
 
 namespace {
 
+// The matrix-core backward: 16-bit inputs, d = 32, windows up to
+// NA2D_BWD_MFMA_MAX_KSIZE, and one map's fp32 rows (dout: H * W * 128
+// bytes) within the 32-bit byte offsets of its buffer addressing. Anything
+// else runs on the VALU kernels, which use 64-bit element offsets.
+bool bwd_mfma_supports(int H, int W, int d, int ksize, int dtype)
+{
+    return (dtype == NA2D_F16 || dtype == NA2D_BF16) && d == 32 &&
+           ksize <= NA2D_BWD_MFMA_MAX_KSIZE && (uint64_t)H * W * d * 4 <= 0x7fffffffull;
+}
+
 int check_backward(const void *q, const void *k, const void *v, const float *rpb,
                    const float *out, const float *lse, const float *dout, const float *dq,
                    const float *dk, const float *dv, const float *drpb, const void *ws, int B,
@@ -310,6 +320,16 @@ extern "C" int na2d_backward_check_args(const void *q, const void *k, const void
                           W, d, ksize, dtype);
 }
 
+extern "C" int na2d_backward_select_algo(int H, int W, int d, int ksize, int dtype)
+{
+    if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
+    const Nd n = nd_2d(1, 1, H, W, d, ksize, NA_WINDOW_NA);
+    const int st = check_sizes(n);
+    if (st != NA2D_OK) return st;
+    if (!valu_supports(n)) return NA2D_ERR_UNSUPPORTED;
+    return bwd_mfma_supports(H, W, d, ksize, dtype) ? NA2D_ALGO_MFMA : NA2D_ALGO_VALU;
+}
+
 extern "C" long long na2d_backward_workspace_bytes(int B, int heads, int H, int W, int ksize)
 {
     if (B <= 0 || heads <= 0 || H <= 0 || W <= 0 || ksize < 1 || ksize > NA2D_VALU_MAX_KSIZE)
@@ -325,8 +345,10 @@ extern "C" int na2d_backward(const void *q, const void *k, const void *v, const 
     const int st = check_backward(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, workspace, B,
                                   heads, H, W, d, ksize, dtype);
     if (st != NA2D_OK) return st;
-    const na2d::BwdProblem p{q,  k,    v,         rpb, out, lse,   dout, dq, dk,
-                             dv, drpb, workspace, B,   heads, H, W, d, ksize, dtype};
+    const int algo =
+        bwd_mfma_supports(H, W, d, ksize, dtype) ? NA2D_ALGO_MFMA : NA2D_ALGO_VALU;
+    const na2d::BwdProblem p{q,  k,    v,         rpb, out, lse,   dout,  dq,   dk, dv,
+                             drpb, workspace, B,   heads, H, W, d, ksize, dtype, algo};
     const hipError_t e = na2d::launch_backward(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         g_last_error = hipGetErrorString(e);
@@ -356,3 +378,5 @@ extern "C" const char *na2d_strerror(int status)
 extern "C" const char *na2d_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" int na2d_version(void) { return kVersion; }
+
+extern "C" long long na2d_occupancy_queries(void) { return na2d::occupancy_queries(); }

@@ -279,8 +279,7 @@ hipError_t launch_bwd_typed(const BwdProblem &p, hipStream_t stream)
     if (blocks == 0 || xcd_grid(blocks) > 0x7fffffffull) return hipErrorInvalidConfiguration;
     a.nblocks = (unsigned)blocks;
     // both passes run on the matrix cores where they apply
-    if (!std::is_same<T, float>::value && D == 32 && p.ksize <= NA2D_BWD_MFMA_MAX_KSIZE)
-        return launch_backward_mfma(p, stream);
+    if (p.algo == NA2D_ALGO_MFMA) return launch_backward_mfma(p, stream);
     if (p.drpb) {  // the bias gradient accumulates: clear it first (a kernel, not a memset)
         const int n = p.heads * (2 * p.ksize - 1) * (2 * p.ksize - 1);
         hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p.drpb, n);

@@ -25,6 +25,7 @@ struct BwdProblem {
     float *dq, *dk, *dv, *drpb;
     void *workspace;
     int B, heads, H, W, d, ksize, dtype;
+    int algo;  // NA2D_ALGO_MFMA: both passes on the matrix cores; NA2D_ALGO_VALU
 };
 
 // The backward workspace: per query its softmax statistics (a float2), then,
@@ -52,5 +53,9 @@ hipError_t launch_mfma_1d(const Problem &p, hipStream_t stream);  // NA1D
 hipError_t launch_mfma_3d(const Problem &p, hipStream_t stream);  // other NA windows (3D, rectangular 2D)
 hipError_t launch_backward(const BwdProblem &p, hipStream_t stream);
 hipError_t launch_backward_mfma(const BwdProblem &p, hipStream_t stream);  // both passes on MFMA
+
+// Occupancy queries made so far in this process (each kernel, device and LDS
+// size is queried once, then cached).
+long long occupancy_queries();
 
 }  // namespace na2d

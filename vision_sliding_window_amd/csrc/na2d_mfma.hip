@@ -53,7 +53,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
+#include <mutex>
+#include <vector>
 
 namespace na2d {
 namespace {
@@ -1139,6 +1142,43 @@ int device_cus()
     return cached_cus;
 }
 
+// Resident workgroups per CU of kernel `f` with `threads` threads and `lds`
+// bytes of dynamic LDS on the current device. The occupancy query -- and,
+// above 64 KB of LDS, the attribute that allows it -- runs once per kernel,
+// device and LDS size; later calls read the answer from a process-wide
+// table, so a forward call makes no HIP call besides its launch.
+struct OccEntry {
+    const void *f;
+    int dev, threads;
+    size_t lds;
+    int per_cu;
+};
+std::mutex g_occ_mutex;
+std::vector<OccEntry> g_occ;
+std::atomic<long long> g_occ_queries{0};
+
+hipError_t occupancy(const void *f, int threads, size_t lds, int &per_cu)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_occ_mutex);
+    for (const OccEntry &o : g_occ)
+        if (o.f == f && o.dev == dev && o.threads == threads && o.lds == lds) {
+            per_cu = o.per_cu;
+            return hipSuccess;
+        }
+    if (lds > 64 * 1024) {
+        e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, threads, lds);
+    g_occ_queries.fetch_add(1);
+    if (e != hipSuccess) return e;
+    g_occ.push_back(OccEntry{f, dev, threads, lds, per_cu});
+    return hipSuccess;
+}
+
 // Arguments and tile counts for a tile shape S; false if the tile list does
 // not fit 32 bits.
 template <typename S, int QY, int RPC>
@@ -1172,13 +1212,8 @@ template <typename K>
 hipError_t launch_persistent(K kern, Args &a, int threads, size_t lds, hipStream_t stream,
                              bool flat = false)
 {
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds);
+    const hipError_t e = occupancy(reinterpret_cast<const void *>(kern), threads, lds, per_cu);
     if (e != hipSuccess) return e;
     const int cus = device_cus();
     if (per_cu <= 0 || cus <= 0) return hipErrorInvalidConfiguration;
@@ -1234,7 +1269,7 @@ hipError_t launch_ring(const Problem &p, hipStream_t stream)
     if (!make_args<S, 2, 8>(p, a)) return hipErrorInvalidConfiguration;
     const auto kern = na2d_mfma_ring_kernel<T, KS, WM, LSE>;
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0);
+    const hipError_t e = occupancy(reinterpret_cast<const void *>(kern), kThreads, 0, per_cu);
     if (e != hipSuccess) return e;
     const int cus = device_cus();
     if (per_cu <= 0 || cus <= 0) return hipErrorInvalidConfiguration;
@@ -1276,6 +1311,8 @@ hipError_t launch_mode(const Problem &p, hipStream_t stream)
 }
 
 }  // namespace
+
+long long occupancy_queries() { return g_occ_queries.load(); }
 
 hipError_t launch_mfma(const Problem &p, hipStream_t stream)
 {

@@ -35,7 +35,8 @@ EXPORTS = ["na2d_forward", "na2d_forward_ex", "na2d_forward_lse", "na2d_check_ar
            "na_select_algo_nd",
            "na2d_strerror", "na2d_last_error", "na2d_version", "na_forward_nd",
            "na_check_args_nd", "na1d_forward", "na3d_forward", "sasa2d_forward",
-           "na2d_backward", "na2d_backward_workspace_bytes", "na2d_backward_check_args"]
+           "na2d_backward", "na2d_backward_workspace_bytes", "na2d_backward_check_args",
+           "na2d_backward_select_algo", "na2d_occupancy_queries", "na_stream_reference"]
 
 TORCH_DTYPE_CODE = {torch.float32: NA2D_F32, torch.float16: NA2D_F16, torch.bfloat16: NA2D_BF16}
 
@@ -94,6 +95,12 @@ def load() -> ctypes.CDLL:
         lib.na2d_backward_workspace_bytes.restype = ctypes.c_longlong
         lib.na2d_backward_check_args.argtypes = [P] * 12 + [I] * 7
         lib.na2d_backward_check_args.restype = I
+        lib.na2d_backward_select_algo.argtypes = [I] * 5
+        lib.na2d_backward_select_algo.restype = I
+        lib.na2d_occupancy_queries.argtypes = []
+        lib.na2d_occupancy_queries.restype = ctypes.c_longlong
+        lib.na_stream_reference.argtypes = [P, P, P, P, ctypes.c_longlong, P]
+        lib.na_stream_reference.restype = I
         _lib = lib
     return _lib
 
@@ -189,6 +196,19 @@ def na2d_backward_check_args(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, wor
     return load().na2d_backward_check_args(*(_addr(t) for t in (q, k, v, rpb, out, lse, dout, dq,
                                                                 dk, dv, drpb, workspace)),
                                            B, heads, H, W, d, ksize, dtype)
+
+
+def na2d_backward_select_algo(H, W, d, ksize, dtype) -> int:
+    return load().na2d_backward_select_algo(H, W, d, ksize, dtype)
+
+
+def na2d_occupancy_queries() -> int:
+    return load().na2d_occupancy_queries()
+
+
+def na_stream_reference(a, b, c, out, elems, stream=None) -> int:
+    return load().na_stream_reference(_addr(a), _addr(b), _addr(c), _addr(out), elems,
+                                      _stream(stream))
 
 
 def na2d_strerror(status: int) -> str:
