@@ -82,7 +82,9 @@ enum {
     NA2D_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned                         */
     NA2D_ERR_ALIAS = -7,       /* out overlaps q, k, v or rpb                              */
     NA2D_ERR_HIP = -8,         /* the HIP runtime reported an error at launch              */
-    NA2D_ERR_ALGO = -9         /* algo not one of na2d_algo                                */
+    NA2D_ERR_ALGO = -9,        /* algo not one of na2d_algo                                */
+    NA2D_ERR_SCRATCH = -10     /* na2d_backward_noalloc: the problem needs more workspace
+                                  than NA2D_NOALLOC_SCRATCH_BYTES                          */
 };
 
 /* Largest ksize each kernel family accepts.  d must be 16, 32, 64 or 128 for
@@ -226,6 +228,29 @@ int na2d_backward_select_algo(int H, int W, int d, int ksize, int dtype);
 /* Bytes of workspace na2d_backward needs for these sizes and window (0 if
  * they are invalid). */
 long long na2d_backward_workspace_bytes(int B, int heads, int H, int W, int ksize);
+
+/* Size of the fixed device array that na2d_backward_noalloc uses as its
+ * workspace (64 MiB: NAT-Tiny stage 1 needs 3.7 MB, a 448 x 448 map with four
+ * heads 15 MB, eight 128 x 128 maps of four heads at k = 21 59 MB). */
+#define NA2D_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* na2d_backward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The arguments and results are those of na2d_backward without `workspace`:
+ * the workspace is a fixed array of NA2D_NOALLOC_SCRATCH_BYTES in device
+ * memory that the library holds on each GPU it runs on until the process
+ * ends (its address is looked up on the first call on a device).  The call
+ * allocates nothing and calls no allocating routine.  Problems whose
+ * workspace (na2d_backward_workspace_bytes) exceeds that size are rejected
+ * with NA2D_ERR_SCRATCH before anything is launched.  Every call on one GPU
+ * shares that GPU's array and leaves it holding its last contents (nothing
+ * in it needs clearing: each call writes every byte it reads), so calls that
+ * overlap on one GPU -- on different streams, or from different threads
+ * without ordering -- race and give wrong gradients; order them. */
+int na2d_backward_noalloc(const void *q, const void *k, const void *v, const float *rpb,
+                          const float *out, const float *lse, const float *dout, float *dq,
+                          float *dk, float *dv, float *drpb, int B, int heads, int H, int W,
+                          int d, int ksize, int dtype, void *stream);
 
 /* Host-only check of na2d_backward's arguments (no HIP call). */
 int na2d_backward_check_args(const void *q, const void *k, const void *v, const float *rpb,

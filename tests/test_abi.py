@@ -321,3 +321,26 @@ def test_stream_reference_rejects_before_launch():
     assert ref(Q, K, V, OUT, 60) == na2d.NA2D_ERR_SHAPE    # not a multiple of 8
     assert ref(Q + 8, K, V, OUT, 64) == na2d.NA2D_ERR_ALIGN
     assert ref(Q, K, V, OUT + 4, 64) == na2d.NA2D_ERR_ALIGN
+
+
+def test_backward_noalloc_rejects_before_launch():
+    """The allocation-free backward checks its arguments like na2d_backward
+    (without a workspace) and refuses, before any HIP call, a problem whose
+    workspace would not fit the fixed device array."""
+    DQ, DK, DV, DRPB, DOUT = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xa0000000
+    f = na2d.na2d_backward_noalloc
+    args = (Q, K, V, RPB, OUT, None, DOUT, DQ, DK, DV, DRPB)
+    assert f(*args, 2, 2, 14, 15, 32, 8, na2d.NA2D_F16, None) == na2d.NA2D_ERR_KSIZE
+    assert f(Q, K, V, RPB, OUT, None, None, DQ, DK, DV, DRPB, 2, 2, 14, 15, 32, 7,
+             na2d.NA2D_F16, None) == na2d.NA2D_ERR_NULL
+    assert f(Q, K, V, RPB, OUT, None, DOUT, DQ, DK, DV, None, 2, 2, 14, 15, 32, 7,
+             na2d.NA2D_F16, None) == na2d.NA2D_ERR_NULL
+    assert f(Q, K, V, RPB, OUT, None, DOUT, Q, DK, DV, DRPB, 2, 2, 14, 15, 32, 7,
+             na2d.NA2D_F16, None) == na2d.NA2D_ERR_ALIAS
+    # 64 maps of 128 x 128 at k = 21: 8 + 41^2 * 4 / 64 bytes per query, past 64 MiB
+    big = na2d.na2d_backward_workspace_bytes(16, 4, 128, 128, 21)
+    assert big > na2d.NA2D_NOALLOC_SCRATCH_BYTES
+    assert f(*args, 16, 4, 128, 128, 32, 21, na2d.NA2D_BF16, None) == na2d.NA2D_ERR_SCRATCH
+    assert "scratch" in na2d.na2d_strerror(na2d.NA2D_ERR_SCRATCH)
+    # the large-kernel workload fits: 8 maps of four heads at k = 21
+    assert na2d.na2d_backward_workspace_bytes(8, 4, 128, 128, 21) <= na2d.NA2D_NOALLOC_SCRATCH_BYTES

@@ -278,10 +278,11 @@ bool bwd_mfma_supports(int H, int W, int d, int ksize, int dtype)
 int check_backward(const void *q, const void *k, const void *v, const float *rpb,
                    const float *out, const float *lse, const float *dout, const float *dq,
                    const float *dk, const float *dv, const float *drpb, const void *ws, int B,
-                   int heads, int H, int W, int d, int ksize, int dtype)
+                   int heads, int H, int W, int d, int ksize, int dtype, bool need_ws = true)
 {
     if (dtype != NA2D_F32 && dtype != NA2D_F16 && dtype != NA2D_BF16) return NA2D_ERR_DTYPE;
-    if (!q || !k || !v || !out || !dout || !dq || !dk || !dv || !ws) return NA2D_ERR_NULL;
+    if (!q || !k || !v || !out || !dout || !dq || !dk || !dv || (!ws && need_ws))
+        return NA2D_ERR_NULL;
     if (!rpb != !drpb) return NA2D_ERR_NULL;  // a bias gradient exactly when there is a bias
     const Nd n = nd_2d(B, heads, H, W, d, ksize, NA_WINDOW_NA);
     const int st = check_sizes(n);
@@ -357,6 +358,33 @@ extern "C" int na2d_backward(const void *q, const void *k, const void *v, const 
     return NA2D_OK;
 }
 
+extern "C" int na2d_backward_noalloc(const void *q, const void *k, const void *v,
+                                     const float *rpb, const float *out, const float *lse,
+                                     const float *dout, float *dq, float *dk, float *dv,
+                                     float *drpb, int B, int heads, int H, int W, int d,
+                                     int ksize, int dtype, void *stream)
+{
+    const int st = check_backward(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, nullptr, B,
+                                  heads, H, W, d, ksize, dtype, false);
+    if (st != NA2D_OK) return st;
+    if (na2d::bwd_workspace_bytes(B, heads, H, W, ksize) > NA2D_NOALLOC_SCRATCH_BYTES)
+        return NA2D_ERR_SCRATCH;
+    void *ws = nullptr;
+    hipError_t e = na2d::noalloc_scratch(&ws);
+    if (e == hipSuccess) {
+        const int algo =
+            bwd_mfma_supports(H, W, d, ksize, dtype) ? NA2D_ALGO_MFMA : NA2D_ALGO_VALU;
+        const na2d::BwdProblem p{q,  k,  v,  rpb,   out,   lse, dout, dq,    dk,    dv,
+                                 drpb, ws, B,  heads, H, W, d,   ksize, dtype, algo};
+        e = na2d::launch_backward(p, static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) {
+        g_last_error = hipGetErrorString(e);
+        return NA2D_ERR_HIP;
+    }
+    return NA2D_OK;
+}
+
 extern "C" const char *na2d_strerror(int status)
 {
     switch (status) {
@@ -371,6 +399,9 @@ extern "C" const char *na2d_strerror(int status)
     case NA2D_ERR_ALIAS: return "out overlaps q, k, v or rpb";
     case NA2D_ERR_HIP: return "HIP runtime error (see na2d_last_error)";
     case NA2D_ERR_ALGO: return "algo must be NA2D_ALGO_AUTO, NA2D_ALGO_VALU or NA2D_ALGO_MFMA";
+    case NA2D_ERR_SCRATCH:
+        return "the backward needs more workspace than the fixed device scratch array holds "
+               "(NA2D_NOALLOC_SCRATCH_BYTES); call na2d_backward with a workspace";
     default: return "unknown status";
     }
 }

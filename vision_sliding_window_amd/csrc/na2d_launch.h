@@ -54,6 +54,10 @@ hipError_t launch_mfma_3d(const Problem &p, hipStream_t stream);  // other NA wi
 hipError_t launch_backward(const BwdProblem &p, hipStream_t stream);
 hipError_t launch_backward_mfma(const BwdProblem &p, hipStream_t stream);  // both passes on MFMA
 
+// Device address of this device's fixed scratch array (na2d_noalloc.hip),
+// looked up on the first call per device and kept.
+hipError_t noalloc_scratch(void **ptr);
+
 // Occupancy queries made so far in this process (each kernel, device and LDS
 // size is queried once, then cached).
 long long occupancy_queries();

@@ -29,6 +29,8 @@ NA2D_ERR_ALIGN = -6
 NA2D_ERR_ALIAS = -7
 NA2D_ERR_HIP = -8
 NA2D_ERR_ALGO = -9
+NA2D_ERR_SCRATCH = -10
+NA2D_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ["na2d_forward", "na2d_forward_ex", "na2d_forward_lse", "na2d_check_args",
            "na2d_select_algo",
@@ -36,7 +38,8 @@ EXPORTS = ["na2d_forward", "na2d_forward_ex", "na2d_forward_lse", "na2d_check_ar
            "na2d_strerror", "na2d_last_error", "na2d_version", "na_forward_nd",
            "na_check_args_nd", "na1d_forward", "na3d_forward", "sasa2d_forward",
            "na2d_backward", "na2d_backward_workspace_bytes", "na2d_backward_check_args",
-           "na2d_backward_select_algo", "na2d_occupancy_queries", "na_stream_reference"]
+           "na2d_backward_select_algo", "na2d_occupancy_queries", "na_stream_reference",
+           "na2d_backward_noalloc"]
 
 TORCH_DTYPE_CODE = {torch.float32: NA2D_F32, torch.float16: NA2D_F16, torch.bfloat16: NA2D_BF16}
 
@@ -101,6 +104,8 @@ def load() -> ctypes.CDLL:
         lib.na2d_occupancy_queries.restype = ctypes.c_longlong
         lib.na_stream_reference.argtypes = [P, P, P, P, ctypes.c_longlong, P]
         lib.na_stream_reference.restype = I
+        lib.na2d_backward_noalloc.argtypes = [P] * 11 + [I] * 7 + [P]
+        lib.na2d_backward_noalloc.restype = I
         _lib = lib
     return _lib
 
@@ -185,6 +190,13 @@ def na2d_backward(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, workspace, B, 
     return load().na2d_backward(*(_addr(t) for t in (q, k, v, rpb, out, lse, dout, dq, dk, dv,
                                                      drpb, workspace)),
                                 B, heads, H, W, d, ksize, dtype, _stream(stream))
+
+
+def na2d_backward_noalloc(q, k, v, rpb, out, lse, dout, dq, dk, dv, drpb, B, heads, H, W, d,
+                          ksize, dtype, stream=None) -> int:
+    return load().na2d_backward_noalloc(*(_addr(t) for t in (q, k, v, rpb, out, lse, dout, dq, dk,
+                                                             dv, drpb)),
+                                        B, heads, H, W, d, ksize, dtype, _stream(stream))
 
 
 def na2d_backward_workspace_bytes(B, heads, H, W, ksize) -> int:
