@@ -115,3 +115,48 @@ def test_auto_selects_mfma_for_16bit():
     assert na2d.na2d_select_algo(56, 56, 32, 7, na2d.NA2D_F16) == MFMA
     assert na2d.na2d_select_algo(56, 56, 32, 7, na2d.NA2D_F32) == VALU
     assert na2d.na2d_select_algo(56, 56, 64, 7, na2d.NA2D_BF16) == VALU
+
+
+def _replace_v(x, v64, dtype):
+    """The inputs with V replaced by v64 rounded to the storage dtype."""
+    import dataclasses
+    from vision_sliding_window_amd.inputs import DTYPES
+    vt = torch.from_numpy(v64).to(DTYPES[dtype])
+    return dataclasses.replace(x, v=vt, v64=vt.double().numpy())
+
+
+@pytest.mark.parametrize("shape,ks", [((1, 2, 45, 38, 32), 21), ((1, 1, 23, 33, 32), 15),
+                                      ((2, 1, 40, 44, 32), 25)], ids=lambda v: str(v))
+def test_bf16_values_past_fp16_range(shape, ks):
+    """bf16 values of V beyond the fp16 range (the wide-window kernel takes V
+    as fp16 where it fits).  (a) V times 2^20: the output scales by exactly
+    2^20, so out / 2^20 is checked against the oracle on the unscaled V at
+    the usual tolerance.  (b) a sparse 0.5% of V's entries times 2^17, so
+    that some rows fit fp16 and some do not: checked against the oracle with
+    the bound that fp16 weights give, 2e-3 + 2^-10 * sum_j p_j |v_j| per
+    element (the sum is the oracle's output for |V|)."""
+    x = make_inputs(shape, ks, "bf16", seed=7, rpb_std=1.0)
+    dev = torch.device("cuda")
+    want = oracle.na2d_forward(x.q64, x.k64, x.v64, x.rpb64, ks)
+    xs = _replace_v(x, x.v64 * 2.0 ** 20, "bf16")
+    got = gpu_forward(xs, ks, MFMA) / 2.0 ** 20
+    assert np.isfinite(got).all()
+    err = np.abs(got - want).max()
+    print("  scaled V: max|err| %.3g" % err, flush=True)
+    assert err <= TOL["bf16"]
+    rng = np.random.default_rng(8)
+    v = x.v64.copy()
+    v[rng.random(v.shape) < 0.005] *= 2.0 ** 17
+    xb = _replace_v(x, v, "bf16")
+    assert np.abs(xb.v64).max() > 65520.0
+    got = gpu_forward(xb, ks, MFMA)
+    assert np.isfinite(got).all()
+    want = oracle.na2d_forward(xb.q64, xb.k64, xb.v64, xb.rpb64, ks)
+    bound = 2e-3 + 2.0 ** -10 * oracle.na2d_forward(xb.q64, xb.k64, np.abs(xb.v64), xb.rpb64, ks)
+    ratio = (np.abs(got - want) / bound).max()
+    print("  sparse large V: max|err| / bound %.3g" % ratio, flush=True)
+    assert ratio <= 1.0
+    # the LSE variant runs the same rows
+    o2, _ = na2d.forward_lse(xb.q.to(dev), xb.k.to(dev), xb.v.to(dev), xb.rpb.to(dev), ks)
+    torch.cuda.synchronize()
+    assert np.array_equal(o2.cpu().double().numpy(), got)

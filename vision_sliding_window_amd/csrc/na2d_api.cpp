@@ -44,15 +44,21 @@ bool is_mfma_1d(const Nd &n)
 
 // The 2D matrix-core kernel (a K/V halo per tile in LDS): square windows, NA
 // up to k = 13 and SASA up to NA2D_MFMA_MAX_KSIZE.  Wider NA windows go to
-// the streaming kernel below: their halos fill the LDS and leave one or two
-// workgroups per CU, and the streaming kernel runs k = 15..25 about 35%
-// faster.
+// the wide-window kernel (na2d_large_mfma.hip), which streams the key blocks
+// of a tile through LDS one block row at a time.
 constexpr int kHaloMaxNaK = 13;
 
 bool is_mfma_2d(const Nd &n)
 {
     return n.D == 1 && n.kd == 1 && n.kh == n.kw && n.kh >= 3 && n.kh <= NA2D_MFMA_MAX_KSIZE &&
            (n.mode == NA_WINDOW_SASA || n.kh <= kHaloMaxNaK);
+}
+
+// The wide-window kernel: square 2D NA windows past the halo kernel's range.
+bool is_mfma_2d_large(const Nd &n)
+{
+    return n.D == 1 && n.kd == 1 && n.kh == n.kw && n.mode == NA_WINDOW_NA && n.kh > kHaloMaxNaK &&
+           n.kh <= NA2D_MFMA_MAX_KSIZE;
 }
 
 // Both take 16-bit inputs with d = 32 and address one (b, h) map with 32-bit
@@ -62,7 +68,7 @@ bool is_mfma_2d(const Nd &n)
 // or rectangular) up to NA2D_MFMA_MAX_KSIZE.
 bool is_mfma_3d(const Nd &n)
 {
-    if (is_mfma_1d(n) || is_mfma_2d(n) || n.mode != NA_WINDOW_NA) return false;
+    if (is_mfma_1d(n) || is_mfma_2d(n) || is_mfma_2d_large(n) || n.mode != NA_WINDOW_NA) return false;
     const int lim = n.kd == 1 ? NA2D_MFMA_MAX_KSIZE : NA3D_MFMA_MAX_KSIZE;
     return n.kd <= NA3D_MFMA_MAX_KSIZE && n.kh <= lim && n.kw <= lim;
 }
@@ -70,7 +76,7 @@ bool is_mfma_3d(const Nd &n)
 bool mfma_supports(const Nd &n, int dtype)
 {
     return (dtype == NA2D_F16 || dtype == NA2D_BF16) && n.d == 32 &&
-           (is_mfma_1d(n) || is_mfma_2d(n) || is_mfma_3d(n)) &&
+           (is_mfma_1d(n) || is_mfma_2d(n) || is_mfma_2d_large(n) || is_mfma_3d(n)) &&
            (uint64_t)n.D * n.H * n.W * n.d * 4 <= 0x7fffffffull;
 }
 
@@ -147,9 +153,10 @@ int forward_nd(const void *q, const void *k, const void *v, const float *rpb, fl
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (resolve_algo(n, dtype, algo) == NA2D_ALGO_MFMA)
-        e = is_mfma_1d(n)   ? na2d::launch_mfma_1d(p, s)
-            : is_mfma_2d(n) ? na2d::launch_mfma(p, s)
-                            : na2d::launch_mfma_3d(p, s);
+        e = is_mfma_1d(n)         ? na2d::launch_mfma_1d(p, s)
+            : is_mfma_2d(n)       ? na2d::launch_mfma(p, s)
+            : is_mfma_2d_large(n) ? na2d::launch_mfma_large(p, s)
+                                  : na2d::launch_mfma_3d(p, s);
     else
         e = na2d::launch_valu(p, s);
     if (e != hipSuccess) {

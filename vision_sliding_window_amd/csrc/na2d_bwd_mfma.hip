@@ -38,7 +38,6 @@ namespace {
 constexpr int kBW = 4;         // waves per workgroup (independent: no barrier in the loops)
 constexpr int kBT = 64 * kBW;  // threads per workgroup
 
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 __device__ inline floatx4 mfma16x16x16(const v4i16 &a, const v4i16 &b, const floatx4 &c, _Float16)
 {

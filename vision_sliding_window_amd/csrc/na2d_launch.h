@@ -51,12 +51,20 @@ hipError_t launch_valu(const Problem &p, hipStream_t stream);
 hipError_t launch_mfma(const Problem &p, hipStream_t stream);     // square 2D windows
 hipError_t launch_mfma_1d(const Problem &p, hipStream_t stream);  // NA1D
 hipError_t launch_mfma_3d(const Problem &p, hipStream_t stream);  // other NA windows (3D, rectangular 2D)
+hipError_t launch_mfma_large(const Problem &p, hipStream_t stream);  // wide square 2D NA windows
 hipError_t launch_backward(const BwdProblem &p, hipStream_t stream);
 hipError_t launch_backward_mfma(const BwdProblem &p, hipStream_t stream);  // both passes on MFMA
 
 // Device address of this device's fixed scratch array (na2d_noalloc.hip),
 // looked up on the first call per device and kept.
 hipError_t noalloc_scratch(void **ptr);
+
+// Compute units of the current device (cached per thread).
+int device_cus();
+// Resident workgroups per CU of kernel `f` with `threads` threads and `lds`
+// bytes of dynamic LDS on the current device, queried once per kernel,
+// device and LDS size and then read from a process-wide cache.
+hipError_t occupancy(const void *f, int threads, size_t lds, int &per_cu);
 
 // Occupancy queries made so far in this process (each kernel, device and LDS
 // size is queried once, then cached).

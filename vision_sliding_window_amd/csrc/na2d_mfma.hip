@@ -59,6 +59,61 @@
 #include <vector>
 
 namespace na2d {
+
+int device_cus()
+{
+    static thread_local int cached_dev = -1, cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
+}
+
+// Resident workgroups per CU of kernel `f` with `threads` threads and `lds`
+// bytes of dynamic LDS on the current device. The occupancy query -- and,
+// above 64 KB of LDS, the attribute that allows it -- runs once per kernel,
+// device and LDS size; later calls read the answer from a process-wide
+// table, so a forward call makes no HIP call besides its launch.
+namespace {
+struct OccEntry {
+    const void *f;
+    int dev, threads;
+    size_t lds;
+    int per_cu;
+};
+std::mutex g_occ_mutex;
+std::vector<OccEntry> g_occ;
+std::atomic<long long> g_occ_queries{0};
+}  // namespace
+
+hipError_t occupancy(const void *f, int threads, size_t lds, int &per_cu)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_occ_mutex);
+    for (const OccEntry &o : g_occ)
+        if (o.f == f && o.dev == dev && o.threads == threads && o.lds == lds) {
+            per_cu = o.per_cu;
+            return hipSuccess;
+        }
+    if (lds > 64 * 1024) {
+        e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, threads, lds);
+    g_occ_queries.fetch_add(1);
+    if (e != hipSuccess) return e;
+    g_occ.push_back(OccEntry{f, dev, threads, lds, per_cu});
+    return hipSuccess;
+}
+
 namespace {
 
 constexpr int kWaves = 4;     // waves per workgroup of the general kernel, stacked vertically
@@ -721,21 +776,6 @@ __device__ inline void issue_out(const Args &a, const Tile &t, int wave, int lan
     }
 }
 
-// Issue priority of a persistent workgroup from the tiles it has left
-// (this one included): 3 while more than three remain, then 2, 1, 0. The
-// sequencer issues from the oldest wave among equals, so without this the
-// youngest workgroup on a CU falls behind the others all the way and runs
-// its last tiles nearly alone; with it a workgroup that is ahead yields.
-// Measured at NAT-Tiny stage 1: -0.4 to -0.5 us (the opposite order: +0.5).
-__device__ inline void work_priority(unsigned end, unsigned tile, unsigned step)
-{
-    const unsigned left = (end - tile + step - 1) / step;
-    if (left > 3) __builtin_amdgcn_s_setprio(3);
-    else if (left == 3) __builtin_amdgcn_s_setprio(2);
-    else if (left == 2) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-}
-
 // Persistent workgroups.  Workgroup w takes every G-th tile of its range (the
 // whole tile list, or with xcd_split its XCD's eighth of it, so the
 // workgroups sharing an L2 work on neighbouring tiles).  Per tile: attend,
@@ -1148,58 +1188,6 @@ na2d_mfma_ring_kernel(Args a)
         }
         __syncthreads();  // the entering rows are visible
     }
-}
-
-int device_cus()
-{
-    static thread_local int cached_dev = -1, cached_cus = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (dev != cached_dev) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        cached_dev = dev;
-        cached_cus = cus;
-    }
-    return cached_cus;
-}
-
-// Resident workgroups per CU of kernel `f` with `threads` threads and `lds`
-// bytes of dynamic LDS on the current device. The occupancy query -- and,
-// above 64 KB of LDS, the attribute that allows it -- runs once per kernel,
-// device and LDS size; later calls read the answer from a process-wide
-// table, so a forward call makes no HIP call besides its launch.
-struct OccEntry {
-    const void *f;
-    int dev, threads;
-    size_t lds;
-    int per_cu;
-};
-std::mutex g_occ_mutex;
-std::vector<OccEntry> g_occ;
-std::atomic<long long> g_occ_queries{0};
-
-hipError_t occupancy(const void *f, int threads, size_t lds, int &per_cu)
-{
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_occ_mutex);
-    for (const OccEntry &o : g_occ)
-        if (o.f == f && o.dev == dev && o.threads == threads && o.lds == lds) {
-            per_cu = o.per_cu;
-            return hipSuccess;
-        }
-    if (lds > 64 * 1024) {
-        e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, threads, lds);
-    g_occ_queries.fetch_add(1);
-    if (e != hipSuccess) return e;
-    g_occ.push_back(OccEntry{f, dev, threads, lds, per_cu});
-    return hipSuccess;
 }
 
 // Arguments and tile counts for a tile shape S; false if the tile list does
