@@ -107,6 +107,12 @@ __host__ __device__ constexpr int col_pitch(int ks)
 __host__ __device__ constexpr int col_floats(int ks) { return 2 * ks * col_pitch(ks); }
 __host__ __device__ constexpr int raw_floats(int ks) { return (2 * ks - 1) * (2 * ks - 1) + 2 * ks + 16; }
 constexpr int kRawPad = 4;
+// The column mask of a wave whose windows are clamped on the column axis:
+// entry kMaskPad + i is 0 for window column i in [0, ksize), else -inf, for
+// i from the first column of the wave's blocks (at most 6 before a window's
+// first: 3 from aligning the blocks, 3 across the subtile) to its last
+// (4 kLMaxBlocks - 1 past a window's first at most).
+constexpr int kMaskPad = 8;
 
 // Where one tile sits (uniform values).
 struct LTile {
@@ -293,11 +299,13 @@ __device__ inline half4 p_half4(const float *p)
 // update, and the products with V (fp16 in LDS). CLAMP: the wave has fewer
 // than NB blocks (ncb < NB); blocks past its last read its last block's keys
 // and values and get a -inf bias. COLCLAMP: the wave's queries' windows are
-// clamped on the column axis; each score is masked by its query's window.
+// clamped on the column axis; each query's window columns are masked by
+// adding `cmask` (0 inside the window, -inf outside) to the bias.
 template <typename T, int NB, bool CLAMP, bool COLCLAMP, bool LSE>
 __device__ inline void lwave_row(const LArgs &a, const LTile &t, int rb, int lane,
                                  const typename Frag<T>::type &qf, const unsigned char *kbuf,
-                                 const unsigned char *vbuf, const float *table, LWave &w)
+                                 const unsigned char *vbuf, const float *table, const float *cmask,
+                                 LWave &w)
 {
     using FragT = typename Frag<T>::type;
     const int ks = a.ks, nb = 2 * ks - 1;
@@ -310,6 +318,7 @@ __device__ inline void lwave_row(const LArgs &a, const LTile &t, int rb, int lan
     else
         brow = (rowin ? ky - w.qy + ks - 1 : nb) * col_pitch(ks);
     lds_cf32 *bp = (lds_cf32 *)table + brow + w.bcol;
+    lds_cf32 *mp = (lds_cf32 *)cmask + kMaskPad + w.cxw;
     const unsigned char *kb = kbuf + (unsigned)w.cb0 * 1024u + stage_off(g, c);
     const unsigned char *vb = vbuf + (unsigned)w.cb0 * 1024u;
     float sc[NB][4];
@@ -319,17 +328,14 @@ __device__ inline void lwave_row(const LArgs &a, const LTile &t, int rb, int lan
         const FragT kf = __builtin_bit_cast(FragT, *(lds_cu4 *)(kb + (unsigned)jj * 1024u));
         floatx4 bias;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bias[e] = bp[4 * j + e];
-        const floatx4 acc = mfma16x16x32(kf, qf, bias);  // q.k + B
-#pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if constexpr (COLCLAMP) {
-                const bool in = (unsigned)(w.cxw + 4 * j + e) < (unsigned)ks;
-                sc[j][e] = in ? acc[e] : -__builtin_inff();
-            } else {
-                sc[j][e] = acc[e];  // the table holds -inf outside the window
-            }
+            bias[e] = bp[4 * j + e];
+            if constexpr (COLCLAMP) bias[e] += mp[4 * j + e];
         }
+        // q.k + B, -inf outside the query's window
+        const floatx4 acc = mfma16x16x32(kf, qf, bias);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[j][e] = acc[e];
     }
     // online softmax over this row's blocks (log2 units; the scores are not
     // yet scaled, and c > 0 makes the scaled max the max of the scaled ones)
@@ -345,7 +351,7 @@ __device__ inline void lwave_row(const LArgs &a, const LTile &t, int rb, int lan
     // which after a query's first window row is rare. The result is the same
     // for any reference; m = -inf (no key of the query seen yet) always moves.
     if (__builtin_amdgcn_ballot_w64(mc > w.m + 8.f)) {
-        const float mnew = fmaxf(w.m, mc);
+        const float mnew = max_f32(w.m, mc);
         const float corr = __builtin_amdgcn_exp2f(w.m - (mnew == -__builtin_inff() ? 0.f : mnew));
         w.l = w.l * corr;  // corr = 0 while m = -inf: nothing accumulated yet
         if constexpr (LSE) w.lex *= corr;
@@ -402,34 +408,13 @@ __device__ inline void lwave_row(const LArgs &a, const LTile &t, int rb, int lan
     }
 }
 
-// A block row with as few blocks as the wave needs: NBW blocks cover any
-// alignment of its windows in the block grid, NBW - 1 the aligned case;
-// fewer (at the map's borders) run the NBW - 1 loop with its last blocks
-// masked.
-template <typename T, int NBW, bool COLCLAMP, bool LSE>
-__device__ inline void lwave_row_n(const LArgs &a, const LTile &t, int rb, int lane,
-                                   const typename Frag<T>::type &qf, const unsigned char *kbuf,
-                                   const unsigned char *vbuf, const float *table, LWave &w)
-{
-    if (w.ncb == NBW)
-        lwave_row<T, NBW, false, COLCLAMP, LSE>(a, t, rb, lane, qf, kbuf, vbuf, table, w);
-    else if (w.ncb == NBW - 1)
-        lwave_row<T, NBW - 1, false, COLCLAMP, LSE>(a, t, rb, lane, qf, kbuf, vbuf, table, w);
-    else
-        lwave_row<T, NBW - 1, true, COLCLAMP, LSE>(a, t, rb, lane, qf, kbuf, vbuf, table, w);
-}
-
-template <typename T, int NBW, bool LSE>
-__device__ inline void lwave_row_any(const LArgs &a, const LTile &t, int rb, int lane,
-                                     const typename Frag<T>::type &qf, const unsigned char *kbuf,
-                                     const unsigned char *vbuf, const float *raw, const float *col,
-                                     LWave &w)
-{
-    if (w.colclamp)
-        lwave_row_n<T, NBW, true, LSE>(a, t, rb, lane, qf, kbuf, vbuf, raw, w);
-    else
-        lwave_row_n<T, NBW, false, LSE>(a, t, rb, lane, qf, kbuf, vbuf, col, w);
-}
+// The kind of a wave's row loop: NB blocks per row, CLAMP and COLCLAMP as
+// in lwave_row.
+template <int NB, bool CLAMP, bool COLCLAMP>
+struct RowKind {
+    static constexpr int nb = NB;
+    static constexpr bool clamp = CLAMP, colclamp = COLCLAMP;
+};
 
 // out = O / sum for the wave's queries (lane (g, c): dims 16 dh + 4 g + j of
 // query c), non-temporal; with LSE, lane g == 0 also writes ln(sum of
@@ -470,6 +455,7 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
     __shared__ float raw_area[kRawPad + kRawMax];
     float *const raw = raw_area + kRawPad;
     __shared__ float col[kColMax];
+    __shared__ float cmask[kMaskPad + 4 * kLMaxBlocks];
     // per tile parity, the sequence number of a tile whose V holds values too
     // large for fp16 (bf16 inputs)
     __shared__ unsigned ovf[2];
@@ -490,6 +476,8 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
     if (tile >= end) return;
 
     if (tid < 2) ovf[tid] = 0u;
+    if (tid < kMaskPad + 4 * kLMaxBlocks)
+        cmask[tid] = (unsigned)(tid - kMaskPad) < (unsigned)a.ks ? 0.f : -__builtin_inff();
     LTile t = ltile(a, tile);
     int bias_head = t.h;
     lstage_bias(a, t.h, raw, col, tid);
@@ -535,25 +523,71 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
         const bool more = next < end;
         LTile tn = t;
         LSlices sn = sl;
-        for (int rb = 0; rb < t.nbr; ++rb) {
-            // the next block row, or the next tile's first, loads while this one is used
-            const bool last = rb + 1 == t.nbr;
-            if (last && more) {
-                tn = ltile(a, next);
-                lslices(a, tn, tid, sn);
-                lstage_load(a, tn, sn, 0, st);
-                qraw = load_q(tn);
-            } else if (!last) {
-                lstage_load(a, t, sl, rb + 1, st);
+        // The row loop, compiled once per kind of wave (blocks per row, column
+        // clamping: uniform over the wave and fixed for the tile), so that its
+        // accumulators stay in place from row to row.
+        auto rows = [&](auto kind) {
+            using K = decltype(kind);
+            const float *table = K::colclamp ? raw : col;
+            for (int rb = 0; rb < t.nbr; ++rb) {
+                // The next block row, or the next tile's first with its queries,
+                // loads while this one is used. The loads are issued on every row
+                // (past the end: out of range, which reads nothing) so that they
+                // always land in the same registers: loads issued on two paths
+                // would be merged by copies that wait for them at once.
+                const bool last = rb + 1 == t.nbr;
+                if (last && more) {
+                    tn = ltile(a, next);
+                    lslices(a, tn, tid, sn);
+                }
+                {
+                    const int64_t base = last ? tn.map_base : t.map_base;
+                    const unsigned drow = last ? 0u : (unsigned)(4 * (rb + 1) * a.W) * 64u;
+                    const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, base, kD * 2, map_bytes);
+                    const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, base, kD * 2, map_bytes);
+#pragma unroll
+                    for (int e = 0; e < kLSlices; ++e) {
+                        const unsigned off = last ? (more ? sn.goff[e] : kOutOfRange) : sl.goff[e] + drow;
+                        st.k[e] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+                        st.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+                    }
+                    if (last) {  // the next tile's queries (uniform branch, one load)
+                        const int c = lane & 15, g = lane >> 4;
+                        const int y = min(tn.y0 + 4 * (wave >> 1) + (c >> 2), a.H - 1);
+                        const int x = min(tn.x0 + 4 * (wave & 1) + (c & 3), a.W - 1);
+                        const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, base, kD * 2, map_bytes);
+                        qraw = __builtin_amdgcn_raw_buffer_load_b128(
+                            rq, more ? (unsigned)(y * a.W + x) * 64u + 16u * g : kOutOfRange, 0, kNonTemporal);
+                    }
+                }
+                if (w.active && rb >= w.rb0 && rb <= w.rb1)
+                    lwave_row<T, K::nb, K::clamp, K::colclamp, LSE>(a, t, rb, lane, qf, kbuf[buf], vbuf[buf],
+                                                                    table, cmask, w);
+                if (last) break;
+                // the other buffer was last read before the barrier that ended the previous row
+                __builtin_amdgcn_s_waitcnt(0);
+                stage(buf ^ 1);
+                __syncthreads();
+                buf ^= 1;
             }
-            if (w.active && rb >= w.rb0 && rb <= w.rb1)
-                lwave_row_any<T, NBW, LSE>(a, t, rb, lane, qf, kbuf[buf], vbuf[buf], raw, col, w);
-            if (last) break;
-            // the other buffer was last read before the barrier that ended the previous row
-            __builtin_amdgcn_s_waitcnt(0);
-            stage(buf ^ 1);
-            __syncthreads();
-            buf ^= 1;
+        };
+        // NBW blocks cover any alignment of the wave's windows in the block
+        // grid, NBW - 1 the aligned case; fewer (at the map's borders) run the
+        // NBW - 1 loop with its last blocks masked
+        if (w.colclamp) {
+            if (w.ncb == NBW)
+                rows(RowKind<NBW, false, true>{});
+            else if (w.ncb == NBW - 1)
+                rows(RowKind<NBW - 1, false, true>{});
+            else
+                rows(RowKind<NBW - 1, true, true>{});
+        } else {
+            if (w.ncb == NBW)
+                rows(RowKind<NBW, false, false>{});
+            else if (w.ncb == NBW - 1)
+                rows(RowKind<NBW - 1, false, false>{});
+            else
+                rows(RowKind<NBW - 1, true, false>{});
         }
         if constexpr (!__is_same(T, _Float16)) {
             // Uniform over the workgroup: every row of the tile was staged before

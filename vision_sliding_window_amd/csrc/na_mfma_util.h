@@ -62,12 +62,20 @@ __device__ inline floatx4 mfma16x16x16(const bf16x4 &a, const bf16x4 &b, const f
 // v_permlane16_swap(x, x) returns both members of each (l, l ^ 16) pair in its
 // two results (and likewise permlane32 for l ^ 32), so op(r0, r1) is the
 // pairwise reduction -- the same value, bit for bit, in both lanes.
+// (v_max_f32 written out: fmaxf would first quiet both inputs, two more
+// instructions per step, which a max over scores does not need)
+__device__ inline float max_f32(float a, float b)
+{
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(a), "v"(b));
+    return m;
+}
 __device__ inline float quad_max(float v)
 {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    v = max_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
     r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float quad_sum(float v)
 {
