@@ -46,6 +46,7 @@
 // No ksize^2-wide tensor ever leaves the chip.
 #include "na2d.h"
 #include "na2d_launch.h"
+#include "na_geometry.h"
 #include "na_mfma_util.h"
 
 #include <hip/hip_runtime.h>
@@ -59,7 +60,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kLWaves = 4;
 constexpr int kLThreads = 64 * kLWaves;
-constexpr int kLMaxBlocks = 8;                 // block rows / columns of a tile's union (ksize <= 25)
+constexpr int kLMaxBlocks = kLargeMaxBlocks;   // block rows / columns of a tile's union (ksize <= 25)
 constexpr int kLRowBytes = kLMaxBlocks * 1024;  // one block row of K (or V): blocks x 16 keys x 64 B
 // slices of a block row a thread stages: 4 rows x 4 kLMaxBlocks columns x 4
 // slices = 512 for K, as many for V, over 256 threads
@@ -77,42 +78,8 @@ struct LArgs {
     float c;  // log2(e) / sqrt(d)
 };
 
-__device__ inline int lwin(int i, int ks, int L)
-{
-    int s = i - (ks >> 1);
-    s = s < 0 ? 0 : s;
-    return s > L - ks ? L - ks : s;
-}
-
-// The bias tables (unscaled: the bias enters the QK product's accumulator).
-//  - `col`: rows for key-minus-query row offsets dy in [-(k-1), k-1], then a
-//    -inf row; columns for column offsets dx in [-X, X + 3], X = k/2 + 6:
-//    the bias where |dx| <= k/2, else -inf. It serves every wave whose
-//    queries' windows are not clamped on the column axis: a query's window
-//    columns are then exactly |dx| <= k/2, and a key row outside its window
-//    reads the -inf row. Such a wave's blocks reach k/2 + 6 columns past its
-//    queries (the subtile spans 3, and the block grid, aligned to the
-//    tile's union, may start up to 3 before the subtile's own), and the
-//    blocks a row reads past the wave's last one (see lwave_row) 3 further.
-//    Its pitch is 4 mod 8, so that the 28 entries a wave reads at once (7
-//    row offsets x 4 column offsets) fall in 28 different banks.
-//  - `raw`: the (2k-1)^2 table, then a -inf row long enough for any column a
-//    row reads (the columns past a window reach 2k + 7), for waves clamped
-//    on the column axis, which mask by each query's window.
-__host__ __device__ constexpr int col_extent(int ks) { return (ks >> 1) + 6; }
-__host__ __device__ constexpr int col_pitch(int ks)
-{
-    return (2 * col_extent(ks) + 4 + 3) / 8 * 8 + 4;  // >= the 2X + 4 columns, = 4 mod 8
-}
-__host__ __device__ constexpr int col_floats(int ks) { return 2 * ks * col_pitch(ks); }
-__host__ __device__ constexpr int raw_floats(int ks) { return (2 * ks - 1) * (2 * ks - 1) + 2 * ks + 16; }
-constexpr int kRawPad = 4;
-// The column mask of a wave whose windows are clamped on the column axis:
-// entry kMaskPad + i is 0 for window column i in [0, ksize), else -inf, for
-// i from the first column of the wave's blocks (at most 6 before a window's
-// first: 3 from aligning the blocks, 3 across the subtile) to its last
-// (4 kLMaxBlocks - 1 past a window's first at most).
-constexpr int kMaskPad = 8;
+// The bias tables `col` and `raw`, the column mask and their paddings are
+// described in na_geometry.h.
 
 // Where one tile sits (uniform values).
 struct LTile {
@@ -135,12 +102,11 @@ __device__ inline LTile ltile(const LArgs &a, unsigned t)
     g.map_base = ((int64_t)b * a.heads + g.h) * a.H * a.W;
     g.y0 = 8 * ty;
     g.x0 = 8 * tx;
-    g.uy0 = lwin(g.y0, a.ks, a.H);
-    g.ux0 = lwin(g.x0, a.ks, a.W);
-    const int uy1 = lwin(min(g.y0 + 7, a.H - 1), a.ks, a.H) + a.ks;
-    const int ux1 = lwin(min(g.x0 + 7, a.W - 1), a.ks, a.W) + a.ks;
-    g.nbr = (uy1 - g.uy0 + 3) >> 2;
-    g.nbc = (ux1 - g.ux0 + 3) >> 2;
+    const LargeTileGeom u = large_tile_geometry(g.y0, g.x0, a.ks, a.H, a.W);
+    g.uy0 = u.uy0;
+    g.ux0 = u.ux0;
+    g.nbr = u.nbr;
+    g.nbc = u.nbc;
     return g;
 }
 
@@ -239,14 +205,15 @@ __device__ inline void lstage_write(const int (&lds)[kLSlices], const LStage &st
 // Fill the head's two bias tables (see col_extent).
 __device__ inline void lstage_bias(const LArgs &a, int h, float *raw, float *col, int tid)
 {
-    const int ks = a.ks, nb = 2 * ks - 1, n = nb * nb, r = ks >> 1;
-    const int X = col_extent(ks), P = col_pitch(ks);
+    const int ks = a.ks, nb = 2 * ks - 1, n = nb * nb;
     const float *rb = a.rpb ? a.rpb + (int64_t)h * n : nullptr;
+    // the kRawPad floats before the table are read too (and masked): -inf, so
+    // that no stale LDS value (a NaN) meets the mask
+    if (tid < kRawPad) raw[tid - kRawPad] = -__builtin_inff();
     for (int u = tid; u < raw_floats(ks); u += kLThreads) raw[u] = u < n ? (rb ? rb[u] : 0.f) : -__builtin_inff();
     for (int u = tid; u < col_floats(ks); u += kLThreads) {
-        const int row = u / P, dx = u - row * P - X;
-        col[u] = row >= nb || dx < -r || dx > r ? -__builtin_inff()
-                                                : (rb ? rb[row * nb + dx + ks - 1] : 0.f);
+        const int src = col_entry_source(u, ks);
+        col[u] = src < 0 ? -__builtin_inff() : (rb ? rb[src] : 0.f);
     }
 }
 
@@ -264,23 +231,20 @@ struct LWave {
 
 __device__ inline void lwave_begin(const LArgs &a, const LTile &t, int wave, int lane, LWave &w)
 {
-    const int ks = a.ks, H = a.H, W = a.W, r = ks >> 1;
-    const int ya = t.y0 + 4 * (wave >> 1), xa = t.x0 + 4 * (wave & 1);
-    w.active = ya < H && xa < W;
-    const int yl = min(ya + 3, H - 1), xl = min(xa + 3, W - 1);
-    w.rb0 = (lwin(min(ya, H - 1), ks, H) - t.uy0) >> 2;
-    w.rb1 = (lwin(yl, ks, H) + ks - 1 - t.uy0) >> 2;
-    w.cb0 = (lwin(min(xa, W - 1), ks, W) - t.ux0) >> 2;
-    w.ncb = ((lwin(xl, ks, W) + ks - 1 - t.ux0) >> 2) - w.cb0 + 1;
-    // no query of the wave has its window pushed in on the column axis
-    w.colclamp = !(xa - r >= 0 && xl + r <= W - 1 && xa + 3 < W);
-    const int c = lane & 15;
-    w.qy = min(ya + (c >> 2), H - 1);
-    w.qx = min(xa + (c & 3), W - 1);
-    w.sy = lwin(w.qy, ks, H);
-    const int kx0 = t.ux0 + 4 * w.cb0;  // first key column of the wave's blocks
-    w.cxw = kx0 - lwin(w.qx, ks, W);
-    w.bcol = w.colclamp ? kx0 - w.qx + ks - 1 : kx0 - w.qx + col_extent(ks);
+    const LargeTileGeom tg{t.uy0, t.ux0, t.nbr, t.nbc};
+    const LargeWaveGeom g = large_wave_geometry(tg, t.y0, t.x0, wave, a.ks, a.H, a.W);
+    w.active = g.active;
+    w.colclamp = g.colclamp;
+    w.rb0 = g.rb0;
+    w.rb1 = g.rb1;
+    w.cb0 = g.cb0;
+    w.ncb = g.ncb;
+    const LargeLaneGeom l = large_lane_geometry(tg, g, lane & 15, a.ks, a.H, a.W);
+    w.qy = l.qy;
+    w.qx = l.qx;
+    w.sy = l.sy;
+    w.cxw = l.cxw;
+    w.bcol = l.bcol;
     w.m = -__builtin_inff();
     w.lex = 0.f;
     w.l = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -311,13 +275,7 @@ __device__ inline void lwave_row(const LArgs &a, const LTile &t, int rb, int lan
     const int ks = a.ks, nb = 2 * ks - 1;
     const int g = lane >> 4, c = lane & 15;
     const int ky = t.uy0 + 4 * rb + g;  // this lane's key row
-    const bool rowin = (unsigned)(ky - w.sy) < (unsigned)ks;
-    int brow;                           // the bias table row of key row ky
-    if constexpr (COLCLAMP)
-        brow = rowin ? (ky - w.qy + ks - 1) * nb : nb * nb;
-    else
-        brow = (rowin ? ky - w.qy + ks - 1 : nb) * col_pitch(ks);
-    lds_cf32 *bp = (lds_cf32 *)table + brow + w.bcol;
+    lds_cf32 *bp = (lds_cf32 *)table + large_bias_row(COLCLAMP, ky, w.qy, w.sy, ks) + w.bcol;
     lds_cf32 *mp = (lds_cf32 *)cmask + kMaskPad + w.cxw;
     const unsigned char *kb = kbuf + (unsigned)w.cb0 * 1024u + stage_off(g, c);
     const unsigned char *vb = vbuf + (unsigned)w.cb0 * 1024u;
@@ -455,7 +413,7 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
     __shared__ float raw_area[kRawPad + kRawMax];
     float *const raw = raw_area + kRawPad;
     __shared__ float col[kColMax];
-    __shared__ float cmask[kMaskPad + 4 * kLMaxBlocks];
+    __shared__ float cmask[kMaskFloats];
     // per tile parity, the sequence number of a tile whose V holds values too
     // large for fp16 (bf16 inputs)
     __shared__ unsigned ovf[2];
@@ -476,7 +434,7 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
     if (tile >= end) return;
 
     if (tid < 2) ovf[tid] = 0u;
-    if (tid < kMaskPad + 4 * kLMaxBlocks)
+    if (tid < kMaskFloats)
         cmask[tid] = (unsigned)(tid - kMaskPad) < (unsigned)a.ks ? 0.f : -__builtin_inff();
     LTile t = ltile(a, tile);
     int bias_head = t.h;

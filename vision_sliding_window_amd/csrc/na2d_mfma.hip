@@ -48,6 +48,7 @@
 // No ksize^2-wide tensor ever leaves the chip.
 #include "na2d.h"
 #include "na2d_launch.h"
+#include "na_geometry.h"
 #include "na_mfma_util.h"
 #include "na_xcd.h"
 
@@ -119,21 +120,6 @@ namespace {
 constexpr int kWaves = 4;     // waves per workgroup of the general kernel, stacked vertically
 constexpr int kThreads = 64 * kWaves;
 
-// Start of the window of ks pixels around i on an axis of length L: for NA
-// (WM = NA_WINDOW_NA) the ks nearest pixels, pushed inward at the borders;
-// for SASA (NA_WINDOW_SASA) the window centred on i, reaching into the zero
-// padding past either end.
-template <int WM>
-__device__ inline int window_start(int i, int ks, int L)
-{
-    int s = i - (ks >> 1);
-    if constexpr (WM == NA_WINDOW_NA) {
-        s = s < 0 ? 0 : s;
-        s = s > L - ks ? L - ks : s;
-    }
-    return s;
-}
-
 struct Args {
     const void *q, *k, *v;
     const float *rpb;
@@ -186,13 +172,6 @@ struct Shape {
     static_assert(BPC % 2 == 0, "P.V consumes key blocks in pairs");
 };
 
-// Rows of candidate keys per wave: QY + ks - 1 rounded up to whole chunks.
-__host__ __device__ constexpr int wave_rows(int QY, int RPC, int ks)
-{
-    const int n = QY + ks - 1;
-    return (n + RPC - 1) / RPC * RPC;
-}
-
 // LDS layout: K and V halos as [lr][NC pixels][4 x 16-byte d-slices], then
 // the head's bias tables (see stage_bias):
 //  - class layout: k tables [2k-1][PC] floats, then a -inf strip of
@@ -237,20 +216,11 @@ __device__ inline Tile tile_geometry(const Args &a, unsigned t)
     g.map_base = ((int64_t)b * a.heads + g.h) * a.H * a.W;
     g.y0 = ty * TY;
     g.x0 = tx * TX;
-    // halo rows [hy0, hy0 + hr) hold every window of the tile's rows; LDS has
-    // lr >= hr rows, the ones past the map zero-filled
-    // halo cols [cx, cx + NC) hold the windows of columns x0 .. x0 + TX - 1.
-    // SASA windows are centred, so the halo is too; its rows and columns past
-    // the map are the zero padding (they load as zeros).
-    if constexpr (WM == NA_WINDOW_SASA) {
-        g.hr = TY + a.ks - 1;
-        g.hy0 = g.y0 - (a.ks >> 1);
-        g.cx = g.x0 - (a.ks >> 1);
-    } else {
-        g.hr = min(TY + a.ks - 1, a.H);
-        g.hy0 = min(window_start<WM>(g.y0, a.ks, a.H), a.H - g.hr);
-        g.cx = a.W >= NC ? min(window_start<WM>(g.x0, a.ks, a.W), a.W - NC) : 0;
-    }
+    // the halo: rows [hy0, hy0 + hr), columns [cx, cx + NC) (na_geometry.h)
+    const HaloGeom hg = halo_geometry<TY, NC, WM>(g.y0, g.x0, a.ks, a.H, a.W);
+    g.hy0 = hg.hy0;
+    g.hr = hg.hr;
+    g.cx = hg.cx;
     return g;
 }
 
@@ -672,7 +642,7 @@ __device__ inline void attend_wave(const Args &a, const Tile &t, const unsigned 
     const int ks = KS ? KS : a.ks, H = a.H, W = a.W, r = ks >> 1;
     const int nr = wave_rows(QY, RPC, ks);
     const int y1 = t.y0 + QY * wave;
-    const int ry = max(t.hy0, min(window_start<WM>(min(y1, H - 1), ks, H), t.hy0 + t.hr - nr));
+    const int ry = wave_first_row<WM>(y1, ks, H, t.hy0, t.hr, nr);
     if constexpr (S::CLS) {
         attend<T, QY, QX, NCB, RPC, KS, kClass, WM, CT, LSE, RING>(a, t, smem, btab, lr, wave, ry, lane,
                                                                qf, o, lsum, st);
@@ -1104,7 +1074,7 @@ na2d_mfma_ring_kernel(Args a)
     using S = Shape<QY, QX, NCB, RPC, NW, false>;
     using FragT = typename Frag<T>::type;
     constexpr int NR = wave_rows(QY, RPC, KS);
-    constexpr int LR = S::TY + KS - 1 > NR ? S::TY + KS - 1 : NR;  // rows a tile's halo needs
+    constexpr int LR = halo_lds_rows(S::TY, QY, RPC, KS);  // rows a tile's halo needs
     static_assert(LR < kRing && S::NC == 16, "ring shape");
     constexpr unsigned BF = bias_floats(false, KS, NR, QY, QX, S::NC, RPC);
     __shared__ __align__(16) unsigned char halo[2 * kRing * 16 * 64];  // K ring, then V ring
@@ -1154,8 +1124,9 @@ na2d_mfma_ring_kernel(Args a)
     __syncthreads();
     if (ty0 + 1 < ty1) {
         tn = tile_at(ty0 + 1);
-        nlo = max(t.hy0 + LR, tn.hy0);
-        nhi = tn.hy0 + LR;
+        const RowRange e = ring_entering(t.hy0, tn.hy0, LR);
+        nlo = e.lo;
+        nhi = e.hi;
         load_ring_rows<QY, QX, NW>(a, tn, nlo, nhi, wave, lane, rg);
     }
     for (int ty = ty0;;) {
@@ -1182,8 +1153,9 @@ na2d_mfma_ring_kernel(Args a)
         ++ty;
         if (ty + 1 < ty1) {
             tn = tile_at(ty + 1);
-            nlo = max(t.hy0 + LR, tn.hy0);
-            nhi = tn.hy0 + LR;
+            const RowRange e = ring_entering(t.hy0, tn.hy0, LR);
+            nlo = e.lo;
+            nhi = e.hi;
             load_ring_rows<QY, QX, NW>(a, tn, nlo, nhi, wave, lane, rg);
         }
         __syncthreads();  // the entering rows are visible
@@ -1211,7 +1183,7 @@ bool make_args(const Problem &p, Args &a)
     const uint64_t ntiles = (uint64_t)p.B * p.heads * a.tiles_x * a.tiles_y;
     if (ntiles == 0 || ntiles > 0x7fffffffull) return false;
     a.ntiles = (unsigned)ntiles;
-    a.lr = max(S::TY + p.ksize - 1, wave_rows(QY, RPC, p.ksize));
+    a.lr = halo_lds_rows(S::TY, QY, RPC, p.ksize);
     a.c = 1.4426950408889634f / sqrtf((float)kD);
     return true;
 }
