@@ -33,13 +33,19 @@ ALGOS = {"auto": 0, "valu": 1, "mfma": 2}
 # kernel family -> its source (a committed traffic summary is used only when it
 # was taken on the source as it is now)
 KERNEL_SOURCES = {"na_valu": "na_valu.hip", "na2d_mfma": "na2d_mfma.hip",
+                  "na2d_large_mfma": "na2d_large_mfma.hip",
                   "na1d_mfma": "na1d_mfma.hip", "na3d_mfma": "na3d_mfma.hip",
                   "na2d_bwd": "na2d_bwd_mfma.hip"}
+# NA windows wider than this go to the wide-window kernel (the library's
+# routing, csrc/na2d_api.cpp)
+HALO_MAX_NA_K = 13
 
 
-def kernel_id(op: str, algo: int) -> str:
+def kernel_id(op: str, algo: int, k: int = 7) -> str:
     if algo == 1:
         return "na_valu"
+    if op == "na2d" and k > HALO_MAX_NA_K:
+        return "na2d_large_mfma"
     return {"na1d": "na1d_mfma", "na3d": "na3d_mfma"}.get(op, "na2d_mfma")
 
 
@@ -448,7 +454,7 @@ def main():
     value = w.queries / (ms * 1e-3)
     gbs = set_bytes / (ms * 1e-3) / 1e9
     tflops = algorithmic_flops(w) / (ms * 1e-3) / 1e12
-    traffic = read_traffic(wname, kernel_id(w.op, algo))
+    traffic = read_traffic(wname, kernel_id(w.op, algo, w.k))
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else int(traffic)}
