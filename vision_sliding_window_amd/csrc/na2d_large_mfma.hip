@@ -20,8 +20,7 @@
 //     A.4 -- a query tile and the key tile its windows need on chip -- with
 //     the key tile streamed in rows so that it fits for wide windows).  A
 //     block is stored as 16 keys x 64 bytes, the 16-byte d-slice s of key p
-//     at slot s ^ copy_swz(p): conflict-free for both the K reads and the
-//     transposing V reads below.
+//     at slot s ^ bswz(p) (see bswz).
 //  2. Logits.  Per block, S^T = K_block Q^T is one v_mfma_f32_16x16x32 (d =
 //     32 is the contraction); lane (g, c) then holds query c against the
 //     four keys of block row g.  For a subtile whose queries are all
@@ -81,6 +80,26 @@ struct LArgs {
 // The bias tables `col` and `raw`, the column mask and their paddings are
 // described in na_geometry.h.
 
+// A staged block: 16 keys x 64 bytes, the 16-byte d-slice s of key p at
+// slot s ^ bswz(p). The K reads (lane (g, c): slice g of key c, 16 bytes) are
+// conflict-free under any slot swizzle; the transposing V reads (lane (g, i):
+// 8 bytes of key 4 g + i / 4) measured 22% faster with this one than with the
+// swizzle of the halo kernels' copies (copy_swz).
+__device__ inline unsigned bswz(unsigned p) { return ((p >> 1) & 3u) ^ ((p >> 3) & 1u); }
+__device__ inline unsigned bstage_off(int g, int c)
+{
+    return (unsigned)c * 64u + 16u * ((unsigned)g ^ bswz((unsigned)c));
+}
+// where lane (g, i) reads V^T for dims 16 dh .. 16 dh + 15: dims 16 dh +
+// 4 (i & 3) .. + 3 of key 4 g + (i >> 2); the lane then holds dim 16 dh + i of
+// keys 4 g .. 4 g + 3
+__device__ inline unsigned btr_read_off(int g, int i, int dh)
+{
+    const unsigned p = 4u * g + ((unsigned)i >> 2);
+    const unsigned s = 2u * dh + ((unsigned)(i & 3) >> 1);
+    return p * 64u + 16u * (s ^ bswz(p)) + 8u * (unsigned)(i & 1);
+}
+
 // Where one tile sits (uniform values).
 struct LTile {
     int h;
@@ -124,7 +143,7 @@ __device__ inline int lslice_lds(int tid, int e)
     const int s = tid + kLThreads * e;
     const int px = s >> 2, g = s & 3;
     const int ri = px >> 5, cj = px & 31;
-    return (int)((unsigned)(cj >> 2) * 1024u + stage_off(g, 4 * ri + (cj & 3)));
+    return (int)((unsigned)(cj >> 2) * 1024u + bstage_off(g, 4 * ri + (cj & 3)));
 }
 
 __device__ inline void lslices(const LArgs &a, const LTile &t, int tid, LSlices &sl)
@@ -277,7 +296,7 @@ __device__ inline void lwave_row(const LArgs &a, const LTile &t, int rb, int lan
     const int ky = t.uy0 + 4 * rb + g;  // this lane's key row
     lds_cf32 *bp = (lds_cf32 *)table + large_bias_row(COLCLAMP, ky, w.qy, w.sy, ks) + w.bcol;
     lds_cf32 *mp = (lds_cf32 *)cmask + kMaskPad + w.cxw;
-    const unsigned char *kb = kbuf + (unsigned)w.cb0 * 1024u + stage_off(g, c);
+    const unsigned char *kb = kbuf + (unsigned)w.cb0 * 1024u + bstage_off(g, c);
     const unsigned char *vb = vbuf + (unsigned)w.cb0 * 1024u;
     float sc[NB][4];
 #pragma unroll
@@ -347,9 +366,9 @@ __device__ inline void lwave_row(const LArgs &a, const LTile &t, int rb, int lan
 #pragma unroll
             for (int dh = 0; dh < 2; ++dh) {
                 const v4i16 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16 *)(vb + (unsigned)ja * 1024u + tr_read_off(g, c, dh)));
+                    (lds_v4i16 *)(vb + (unsigned)ja * 1024u + btr_read_off(g, c, dh)));
                 const v4i16 vbb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16 *)(vb + (unsigned)jb * 1024u + tr_read_off(g, c, dh)));
+                    (lds_v4i16 *)(vb + (unsigned)jb * 1024u + btr_read_off(g, c, dh)));
                 const half8 vt = __builtin_bit_cast(half8, __builtin_shufflevector(va, vbb, 0, 1, 2, 3, 4, 5, 6, 7));
                 w.o[dh] = mfma16x16x32(vt, ph, w.o[dh]);
             }
@@ -359,7 +378,7 @@ __device__ inline void lwave_row(const LArgs &a, const LTile &t, int rb, int lan
 #pragma unroll
             for (int dh = 0; dh < 2; ++dh) {
                 const v4i16 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_v4i16 *)(vb + (unsigned)ja * 1024u + tr_read_off(g, c, dh)));
+                    (lds_v4i16 *)(vb + (unsigned)ja * 1024u + btr_read_off(g, c, dh)));
                 w.o[dh] = mfma16x16x16(__builtin_bit_cast(half4, vt), pa, w.o[dh]);
             }
         }
