@@ -37,14 +37,14 @@ KERNEL_SOURCES = {"na_valu": "na_valu.hip", "na2d_mfma": "na2d_mfma.hip",
                   "na1d_mfma": "na1d_mfma.hip", "na3d_mfma": "na3d_mfma.hip",
                   "na2d_bwd": "na2d_bwd_mfma.hip"}
 # NA windows wider than this go to the wide-window kernel (the library's
-# routing, csrc/na2d_api.cpp)
-HALO_MAX_NA_K = 13
+# routing, csrc/na2d_api.cpp: halo_max_na_k)
+HALO_MAX_NA_K = {"f16": 13, "bf16": 9}
 
 
-def kernel_id(op: str, algo: int, k: int = 7) -> str:
+def kernel_id(op: str, algo: int, k: int = 7, dtype: str = "f16") -> str:
     if algo == 1:
         return "na_valu"
-    if op == "na2d" and k > HALO_MAX_NA_K:
+    if op == "na2d" and k > HALO_MAX_NA_K.get(dtype, 13):
         return "na2d_large_mfma"
     return {"na1d": "na1d_mfma", "na3d": "na3d_mfma"}.get(op, "na2d_mfma")
 
@@ -454,7 +454,7 @@ def main():
     value = w.queries / (ms * 1e-3)
     gbs = set_bytes / (ms * 1e-3) / 1e9
     tflops = algorithmic_flops(w) / (ms * 1e-3) / 1e12
-    traffic = read_traffic(wname, kernel_id(w.op, algo, w.k))
+    traffic = read_traffic(wname, kernel_id(w.op, algo, w.k, w.dtype))
     roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else int(traffic)}

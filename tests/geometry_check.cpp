@@ -12,7 +12,7 @@
 //   - the column-run kernel's ring of 16 rows: a tile's halo fits, and after
 //     each step (rows entering the next halo written to slot row & 15) every
 //     row a wave reads sits in its slot;
-//  wide-window kernel:
+//  wide-window kernel (8 x 8 tiles, and 4 x 16 tiles up to k = 17):
 //   - the tile's block grid stages at most kLargeMaxBlocks block columns, and
 //     each wave's block rows and columns hold its queries' windows;
 //   - the row kind the kernel dispatches (blocks per row, clamped or not)
@@ -145,17 +145,31 @@ static void check_ring(int k)
 
 // ---- wide-window kernel
 
-static void check_large(int k)
+// WX waves across a tile of four waves: TY x TX = (16 / WX) x (4 WX) queries
+static void check_large(int k, int WX)
 {
     const int nb = 2 * k - 1, r = k >> 1, P = col_pitch(k), X = col_extent(k);
     const int NBW = (k + 9) / 4;  // blocks per row of the widest kind (the launcher's choice)
+    const int TY = 16 / WX, TX = 4 * WX;
+    // the four waves' 16 lanes place the tile's TY x TX queries once each
+    {
+        std::vector<int> seen(TY * TX, 0);
+        for (int wave = 0; wave < 4; ++wave)
+            for (int c = 0; c < 16; ++c) {
+                const QueryPos q = large_query(0, 0, wave, WX, c);
+                CHECK(q.y >= 0 && q.y < TY && q.x >= 0 && q.x < TX, "large WX=%d wave %d lane %d outside the tile",
+                      WX, wave, c);
+                if (q.y >= 0 && q.y < TY && q.x >= 0 && q.x < TX) ++seen[q.y * TX + q.x];
+            }
+        for (int i = 0; i < TY * TX; ++i) CHECK(seen[i] == 1, "large WX=%d query %d placed %d times", WX, i, seen[i]);
+    }
     for (int L : axis_lengths(k, false)) {
         // rows: block rows of each wave and the bias row of every key row
-        for (int y0 = 0; y0 < L; y0 += 8) {
-            const LargeTileGeom t = large_tile_geometry(y0, 0, k, L, L);
+        for (int y0 = 0; y0 < L; y0 += TY) {
+            const LargeTileGeom t = large_tile_geometry(y0, 0, TY, TX, k, L, L);
             CHECK(t.nbr >= 1, "large k=%d H=%d y0=%d nbr=%d", k, L, y0, t.nbr);
-            for (int wr = 0; wr < 2; ++wr) {
-                const LargeWaveGeom w = large_wave_geometry(t, y0, 0, 2 * wr, k, L, L);
+            for (int wr = 0; wr < 4 / WX; ++wr) {
+                const LargeWaveGeom w = large_wave_geometry(t, y0, 0, WX * wr, WX, k, L, L);
                 if (!w.active) continue;
                 CHECK(0 <= w.rb0 && w.rb0 <= w.rb1 && w.rb1 < t.nbr, "large k=%d H=%d y0=%d rows %d..%d of %d", k, L,
                       y0, w.rb0, w.rb1, t.nbr);
@@ -181,11 +195,11 @@ static void check_large(int k)
             }
         }
         // columns: block columns, row kinds, and the column part of every bias read
-        for (int x0 = 0; x0 < L; x0 += 8) {
-            const LargeTileGeom t = large_tile_geometry(0, x0, k, L, L);
-            CHECK(t.nbc >= 1 && t.nbc <= kLargeMaxBlocks, "large k=%d W=%d x0=%d nbc=%d", k, L, x0, t.nbc);
-            for (int wc = 0; wc < 2; ++wc) {
-                const LargeWaveGeom w = large_wave_geometry(t, 0, x0, wc, k, L, L);
+        for (int x0 = 0; x0 < L; x0 += TX) {
+            const LargeTileGeom t = large_tile_geometry(0, x0, TY, TX, k, L, L);
+            CHECK(t.nbc >= 1 && t.nbc <= kLargeMaxBlocks, "large k=%d WX=%d W=%d x0=%d nbc=%d", k, WX, L, x0, t.nbc);
+            for (int wc = 0; wc < WX; ++wc) {
+                const LargeWaveGeom w = large_wave_geometry(t, 0, x0, wc, WX, k, L, L);
                 if (!w.active) continue;
                 CHECK(w.cb0 >= 0 && w.ncb >= 1 && w.cb0 + w.ncb <= t.nbc && w.ncb <= NBW,
                       "large k=%d W=%d x0=%d wave %d blocks %d+%d of %d", k, L, x0, wc, w.cb0, w.ncb, t.nbc);
@@ -252,7 +266,11 @@ int main()
     check_halo_shape<2, 8, 2, 2, 4, NA_WINDOW_NA>("2x8 ncb2 NA", 15, 25);
     check_halo_shape<2, 8, 2, 2, 4, NA_WINDOW_SASA>("2x8 ncb2 SASA", 15, 25);
     check_ring(7);
-    for (int k = 7; k <= NA2D_MFMA_MAX_KSIZE; k += 2) check_large(k);
+    // the launcher's tile shapes: 4 x 16 while 16 + k - 1 <= 32 columns, else 8 x 8
+    for (int k = 7; k <= NA2D_MFMA_MAX_KSIZE; k += 2) {
+        check_large(k, 2);
+        if (k <= 17) check_large(k, 4);
+    }
     if (g_fails) {
         std::printf("%ld of %ld checks failed\n", g_fails, g_checks);
         return 1;

@@ -53,6 +53,7 @@ MUTANTS = [
     ("ring_row_skipped", "r.lo = hy0 + lr > hy0n ? hy0 + lr : hy0n;",
      "r.lo = hy0 + lr + 1 > hy0n ? hy0 + lr + 1 : hy0n;"),
     ("large_block_columns_short", "g.nbc = (ux1 - g.ux0 + 3) >> 2;", "g.nbc = (ux1 - g.ux0) >> 2;"),
+    ("large_wave_column_order", "q.x = x0 + 4 * (wave % WX) + (c & 3);", "q.x = x0 + 4 * (wave % 2) + (c & 3);"),
     ("large_clamp_test_off_by_one", "w.colclamp = !(w.xa - r >= 0 && xl + r <= W - 1 && w.xa + 3 < W);",
      "w.colclamp = !(w.xa - r >= 0 && xl + r <= W && w.xa + 3 < W);"),
     ("col_table_narrow", "return (ks >> 1) + 6;", "return (ks >> 1) + 5;"),

@@ -43,21 +43,24 @@ bool is_mfma_1d(const Nd &n)
 }
 
 // The 2D matrix-core kernel (a K/V halo per tile in LDS): square windows, NA
-// up to k = 13 and SASA up to NA2D_MFMA_MAX_KSIZE.  Wider NA windows go to
-// the wide-window kernel (na2d_large_mfma.hip), which streams the key blocks
-// of a tile through LDS one block row at a time.
-constexpr int kHaloMaxNaK = 13;
+// up to halo_max_na_k and SASA up to NA2D_MFMA_MAX_KSIZE.  Wider NA windows
+// go to the wide-window kernel (na2d_large_mfma.hip), which streams the key
+// blocks of a tile through LDS one block row at a time. For bf16 inputs that
+// kernel, which multiplies fp16 weights by V converted to fp16 where the halo
+// kernel splits the weights into two bf16 parts, measured faster from k = 11
+// (k = 13: 79.5 against 82.1 us at 8 x 4 x 128^2); for fp16 inputs from k = 15.
+int halo_max_na_k(int dtype) { return dtype == NA2D_BF16 ? 9 : 13; }
 
-bool is_mfma_2d(const Nd &n)
+bool is_mfma_2d(const Nd &n, int dtype)
 {
     return n.D == 1 && n.kd == 1 && n.kh == n.kw && n.kh >= 3 && n.kh <= NA2D_MFMA_MAX_KSIZE &&
-           (n.mode == NA_WINDOW_SASA || n.kh <= kHaloMaxNaK);
+           (n.mode == NA_WINDOW_SASA || n.kh <= halo_max_na_k(dtype));
 }
 
 // The wide-window kernel: square 2D NA windows past the halo kernel's range.
-bool is_mfma_2d_large(const Nd &n)
+bool is_mfma_2d_large(const Nd &n, int dtype)
 {
-    return n.D == 1 && n.kd == 1 && n.kh == n.kw && n.mode == NA_WINDOW_NA && n.kh > kHaloMaxNaK &&
+    return n.D == 1 && n.kd == 1 && n.kh == n.kw && n.mode == NA_WINDOW_NA && n.kh > halo_max_na_k(dtype) &&
            n.kh <= NA2D_MFMA_MAX_KSIZE;
 }
 
@@ -66,9 +69,10 @@ bool is_mfma_2d_large(const Nd &n)
 // The streaming kernel: any other NA window with every axis small enough --
 // 3D windows up to NA3D_MFMA_MAX_KSIZE per axis, 2D windows (kd = 1, square
 // or rectangular) up to NA2D_MFMA_MAX_KSIZE.
-bool is_mfma_3d(const Nd &n)
+bool is_mfma_3d(const Nd &n, int dtype)
 {
-    if (is_mfma_1d(n) || is_mfma_2d(n) || is_mfma_2d_large(n) || n.mode != NA_WINDOW_NA) return false;
+    if (is_mfma_1d(n) || is_mfma_2d(n, dtype) || is_mfma_2d_large(n, dtype) || n.mode != NA_WINDOW_NA)
+        return false;
     const int lim = n.kd == 1 ? NA2D_MFMA_MAX_KSIZE : NA3D_MFMA_MAX_KSIZE;
     return n.kd <= NA3D_MFMA_MAX_KSIZE && n.kh <= lim && n.kw <= lim;
 }
@@ -76,7 +80,7 @@ bool is_mfma_3d(const Nd &n)
 bool mfma_supports(const Nd &n, int dtype)
 {
     return (dtype == NA2D_F16 || dtype == NA2D_BF16) && n.d == 32 &&
-           (is_mfma_1d(n) || is_mfma_2d(n) || is_mfma_2d_large(n) || is_mfma_3d(n)) &&
+           (is_mfma_1d(n) || is_mfma_2d(n, dtype) || is_mfma_2d_large(n, dtype) || is_mfma_3d(n, dtype)) &&
            (uint64_t)n.D * n.H * n.W * n.d * 4 <= 0x7fffffffull;
 }
 
@@ -154,8 +158,8 @@ int forward_nd(const void *q, const void *k, const void *v, const float *rpb, fl
     hipError_t e;
     if (resolve_algo(n, dtype, algo) == NA2D_ALGO_MFMA)
         e = is_mfma_1d(n)         ? na2d::launch_mfma_1d(p, s)
-            : is_mfma_2d(n)       ? na2d::launch_mfma(p, s)
-            : is_mfma_2d_large(n) ? na2d::launch_mfma_large(p, s)
+            : is_mfma_2d(n, dtype)       ? na2d::launch_mfma(p, s)
+            : is_mfma_2d_large(n, dtype) ? na2d::launch_mfma_large(p, s)
                                   : na2d::launch_mfma_3d(p, s);
     else
         e = na2d::launch_valu(p, s);

@@ -6,9 +6,11 @@
 // clamped ksize x ksize window, logits (q.k + B) / sqrt(d), softmax over the
 // window, weighted sum of the values.
 //
-// How.  Persistent workgroups of four waves walk a list of 8 x 8 query
-// tiles; wave w owns the 4 x 4 subtile (w / 2, w % 2) of a tile.  The union
-// of the tile's windows -- at most 7 + ksize rows and columns -- is cut into
+// How.  Persistent workgroups of four waves walk a list of query tiles:
+// 4 x 16 while the union of a tile's windows fits 32 staged columns (k <= 17;
+// every block row of such a tile serves all four waves), else 8 x 8. Wave w
+// owns the 4 x 4 subtile (w / WX, w % WX), WX = 4 or 2 waves across. The
+// union of the tile's windows -- at most 15 + ksize columns -- is cut into
 // 4 x 4 key blocks; for a 4 x 4 subtile 4 x 4 blocks cover the window union
 // most tightly (at ksize = 21, 36 blocks against 44 for 16-key rows).
 //  1. Staging.  The tile's key blocks go through LDS one block row (four key
@@ -59,6 +61,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kLWaves = 4;
 constexpr int kLThreads = 64 * kLWaves;
+// widest rows (NBW) that take 4 x 16 tiles (see launch_large_nbw)
+constexpr int kWideTileMaxNBW = 6;
 constexpr int kLMaxBlocks = kLargeMaxBlocks;   // block rows / columns of a tile's union (ksize <= 25)
 constexpr int kLRowBytes = kLMaxBlocks * 1024;  // one block row of K (or V): blocks x 16 keys x 64 B
 // slices of a block row a thread stages: 4 rows x 4 kLMaxBlocks columns x 4
@@ -109,8 +113,10 @@ struct LTile {
     int nbr, nbc;  // block rows / columns of the union
 };
 
+template <int WX>
 __device__ inline LTile ltile(const LArgs &a, unsigned t)
 {
+    constexpr int TY = 16 / WX, TX = 4 * WX;
     const unsigned tpm = (unsigned)a.tiles_x * a.tiles_y;
     const unsigned per_head = tpm * (unsigned)a.B;
     LTile g;
@@ -119,9 +125,9 @@ __device__ inline LTile ltile(const LArgs &a, unsigned t)
     const unsigned b = rem / tpm, tr = rem - b * tpm;
     const int ty = (int)(tr / a.tiles_x), tx = (int)(tr - (unsigned)ty * a.tiles_x);
     g.map_base = ((int64_t)b * a.heads + g.h) * a.H * a.W;
-    g.y0 = 8 * ty;
-    g.x0 = 8 * tx;
-    const LargeTileGeom u = large_tile_geometry(g.y0, g.x0, a.ks, a.H, a.W);
+    g.y0 = TY * ty;
+    g.x0 = TX * tx;
+    const LargeTileGeom u = large_tile_geometry(g.y0, g.x0, TY, TX, a.ks, a.H, a.W);
     g.uy0 = u.uy0;
     g.ux0 = u.ux0;
     g.nbr = u.nbr;
@@ -248,10 +254,11 @@ struct LWave {
     floatx4 o[2];
 };
 
+template <int WX>
 __device__ inline void lwave_begin(const LArgs &a, const LTile &t, int wave, int lane, LWave &w)
 {
     const LargeTileGeom tg{t.uy0, t.ux0, t.nbr, t.nbc};
-    const LargeWaveGeom g = large_wave_geometry(tg, t.y0, t.x0, wave, a.ks, a.H, a.W);
+    const LargeWaveGeom g = large_wave_geometry(tg, t.y0, t.x0, wave, WX, a.ks, a.H, a.W);
     w.active = g.active;
     w.colclamp = g.colclamp;
     w.rb0 = g.rb0;
@@ -396,13 +403,14 @@ struct RowKind {
 // out = O / sum for the wave's queries (lane (g, c): dims 16 dh + 4 g + j of
 // query c), non-temporal; with LSE, lane g == 0 also writes ln(sum of
 // exp(logits)) of its query.
-template <typename T, bool LSE>
+template <typename T, int WX, bool LSE>
 __device__ inline void lwave_store(const LArgs &a, const LTile &t, int wave, int lane, const LWave &w, float os)
 {
     const float l = w.l[0];
     const float inv = __builtin_amdgcn_rcpf(l) * os;
     const int g = lane >> 4, c = lane & 15;
-    const int y = t.y0 + 4 * (wave >> 1) + (c >> 2), x = t.x0 + 4 * (wave & 1) + (c & 3);
+    const QueryPos qp = large_query(t.y0, t.x0, wave, WX, c);
+    const int y = qp.y, x = qp.x;
     const __amdgpu_buffer_rsrc_t ro =
         map_rsrc(a.out, t.map_base, kD * 4, (unsigned)a.H * a.W * (kD * 4));
     const bool in = y < a.H && x < a.W;
@@ -419,7 +427,7 @@ __device__ inline void lwave_store(const LArgs &a, const LTile &t, int wave, int
     }
 }
 
-template <typename T, int NBW, bool LSE>
+template <typename T, int NBW, int WX, bool LSE>
 __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
 {
     using FragT = typename Frag<T>::type;
@@ -455,7 +463,7 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
     if (tid < 2) ovf[tid] = 0u;
     if (tid < kMaskFloats)
         cmask[tid] = (unsigned)(tid - kMaskPad) < (unsigned)a.ks ? 0.f : -__builtin_inff();
-    LTile t = ltile(a, tile);
+    LTile t = ltile<WX>(a, tile);
     int bias_head = t.h;
     lstage_bias(a, t.h, raw, col, tid);
     LSlices sl;
@@ -465,8 +473,8 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
     const unsigned map_bytes = (unsigned)a.H * a.W * (kD * 2);
     auto load_q = [&](const LTile &tt) {
         const int c = lane & 15, g = lane >> 4;
-        const int y = min(tt.y0 + 4 * (wave >> 1) + (c >> 2), a.H - 1);
-        const int x = min(tt.x0 + 4 * (wave & 1) + (c & 3), a.W - 1);
+        const QueryPos qp = large_query(tt.y0, tt.x0, wave, WX, c);
+        const int y = min(qp.y, a.H - 1), x = min(qp.x, a.W - 1);
         const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, tt.map_base, kD * 2, map_bytes);
         return __builtin_amdgcn_raw_buffer_load_b128(rq, (unsigned)(y * a.W + x) * 64u + 16u * g, 0,
                                                      kNonTemporal);
@@ -494,7 +502,7 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
     while (true) {
         work_priority(end, tile, step);
         LWave w;
-        lwave_begin(a, t, wave, lane, w);
+        lwave_begin<WX>(a, t, wave, lane, w);
         const FragT qf = __builtin_bit_cast(FragT, qraw);
         const unsigned next = tile + step;
         const bool more = next < end;
@@ -514,7 +522,7 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
                 // would be merged by copies that wait for them at once.
                 const bool last = rb + 1 == t.nbr;
                 if (last && more) {
-                    tn = ltile(a, next);
+                    tn = ltile<WX>(a, next);
                     lslices(a, tn, tid, sn);
                 }
                 {
@@ -530,8 +538,8 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
                     }
                     if (last) {  // the next tile's queries (uniform branch, one load)
                         const int c = lane & 15, g = lane >> 4;
-                        const int y = min(tn.y0 + 4 * (wave >> 1) + (c >> 2), a.H - 1);
-                        const int x = min(tn.x0 + 4 * (wave & 1) + (c & 3), a.W - 1);
+                        const QueryPos qp = large_query(tn.y0, tn.x0, wave, WX, c);
+                        const int y = min(qp.y, a.H - 1), x = min(qp.x, a.W - 1);
                         const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, base, kD * 2, map_bytes);
                         qraw = __builtin_amdgcn_raw_buffer_load_b128(
                             rq, more ? (unsigned)(y * a.W + x) * 64u + 16u * g : kOutOfRange, 0, kNonTemporal);
@@ -588,7 +596,7 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
                 continue;
             }
         }
-        if (w.active) lwave_store<T, LSE>(a, t, wave, lane, w, os);
+        if (w.active) lwave_store<T, WX, LSE>(a, t, wave, lane, w, os);
         redo = false;
         os = 1.f;
         if (!more) break;
@@ -608,11 +616,17 @@ __global__ __launch_bounds__(kLThreads) void na2d_large_kernel(LArgs a)
     }
 }
 
-template <typename T, int NBW, bool LSE>
+template <typename T, int NBW, int WX, bool LSE>
 hipError_t launch_large_typed(const LArgs &a0, hipStream_t stream)
 {
     LArgs a = a0;
-    const auto kern = na2d_large_kernel<T, NBW, LSE>;
+    constexpr int TY = 16 / WX, TX = 4 * WX;
+    a.tiles_x = (a.W + TX - 1) / TX;
+    a.tiles_y = (a.H + TY - 1) / TY;
+    const uint64_t ntiles = (uint64_t)a.B * a.heads * a.tiles_x * a.tiles_y;
+    if (ntiles == 0 || ntiles > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    a.ntiles = (unsigned)ntiles;
+    const auto kern = na2d_large_kernel<T, NBW, WX, LSE>;
     int per_cu = 0;
     const hipError_t e = occupancy(reinterpret_cast<const void *>(kern), kLThreads, 0, per_cu);
     if (e != hipSuccess) return e;
@@ -631,17 +645,21 @@ hipError_t launch_large_typed(const LArgs &a0, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Tiles of 4 x 16 queries while their union of windows fits the 32 staged
+// columns (16 + k - 1 <= 32: k <= 17): every block row of such a tile is used
+// by all four waves. Wider windows take 8 x 8 tiles, whose first and last
+// block rows only two waves use.
 template <typename T, bool LSE>
 hipError_t launch_large_nbw(const LArgs &a, hipStream_t stream)
 {
     // blocks a wave's windows touch per block row: (3 + k) columns, aligned
     // anywhere in the tile's block grid
     switch ((a.ks + 9) / 4) {
-    case 4: return launch_large_typed<T, 4, LSE>(a, stream);
-    case 5: return launch_large_typed<T, 5, LSE>(a, stream);
-    case 6: return launch_large_typed<T, 6, LSE>(a, stream);
-    case 7: return launch_large_typed<T, 7, LSE>(a, stream);
-    case 8: return launch_large_typed<T, 8, LSE>(a, stream);
+    case 4: return launch_large_typed<T, 4, kWideTileMaxNBW >= 4 ? 4 : 2, LSE>(a, stream);
+    case 5: return launch_large_typed<T, 5, kWideTileMaxNBW >= 5 ? 4 : 2, LSE>(a, stream);
+    case 6: return launch_large_typed<T, 6, kWideTileMaxNBW >= 6 ? 4 : 2, LSE>(a, stream);
+    case 7: return launch_large_typed<T, 7, 2, LSE>(a, stream);
+    case 8: return launch_large_typed<T, 8, 2, LSE>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -667,11 +685,8 @@ hipError_t launch_mfma_large(const Problem &p, hipStream_t stream)
     a.H = p.H;
     a.W = p.W;
     a.ks = p.ksize;
-    a.tiles_x = (p.W + 7) / 8;
-    a.tiles_y = (p.H + 7) / 8;
-    const uint64_t ntiles = (uint64_t)p.B * p.heads * a.tiles_x * a.tiles_y;
-    if (ntiles == 0 || ntiles > 0x7fffffffull) return hipErrorInvalidConfiguration;
-    a.ntiles = (unsigned)ntiles;
+    a.tiles_x = a.tiles_y = 0;  // per tile shape (launch_large_typed)
+    a.ntiles = 0;
     a.xcd_split = 0;
     a.c = 1.4426950408889634f / sqrtf((float)kD);
     if (p.dtype == NA2D_F16)

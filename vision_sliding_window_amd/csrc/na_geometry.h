@@ -106,8 +106,9 @@ __host__ __device__ inline RowRange ring_entering(int hy0, int hy0n, int lr)
     return r;
 }
 
-// ---- wide-window kernel (na2d_large_mfma.hip): 8 x 8 query tiles, waves of
-// 4 x 4 queries, keys in 4 x 4 blocks
+// ---- wide-window kernel (na2d_large_mfma.hip): tiles of four waves of 4 x 4
+// queries, WX waves across (8 x 8 tiles for WX = 2, 4 x 16 for WX = 4), keys
+// in 4 x 4 blocks
 
 constexpr int kLargeMaxBlocks = 8;  // block columns staged per block row (ksize <= 25)
 
@@ -153,24 +154,40 @@ __host__ __device__ inline int col_entry_source(int u, int ks)
     return row >= nb || dx < -r || dx > r ? -1 : row * nb + dx + ks - 1;
 }
 
-// The union of the windows of the tile whose first query is (y0, x0): key
-// rows from uy0 and columns from ux0, nbr x nbc blocks of 4 x 4 keys.
+// The union of the windows of the TY x TX tile whose first query is (y0,
+// x0): key rows from uy0 and columns from ux0, nbr x nbc blocks of 4 x 4 keys.
 struct LargeTileGeom {
     int uy0, ux0, nbr, nbc;
 };
-__host__ __device__ inline LargeTileGeom large_tile_geometry(int y0, int x0, int ks, int H, int W)
+__host__ __device__ inline LargeTileGeom large_tile_geometry(int y0, int x0, int TY, int TX, int ks, int H, int W)
 {
     LargeTileGeom g;
     g.uy0 = window_start<NA_WINDOW_NA>(y0, ks, H);
     g.ux0 = window_start<NA_WINDOW_NA>(x0, ks, W);
-    const int uy1 = window_start<NA_WINDOW_NA>(y0 + 7 < H - 1 ? y0 + 7 : H - 1, ks, H) + ks;
-    const int ux1 = window_start<NA_WINDOW_NA>(x0 + 7 < W - 1 ? x0 + 7 : W - 1, ks, W) + ks;
+    const int yl = y0 + TY - 1 < H - 1 ? y0 + TY - 1 : H - 1;
+    const int xl = x0 + TX - 1 < W - 1 ? x0 + TX - 1 : W - 1;
+    const int uy1 = window_start<NA_WINDOW_NA>(yl, ks, H) + ks;
+    const int ux1 = window_start<NA_WINDOW_NA>(xl, ks, W) + ks;
     g.nbr = (uy1 - g.uy0 + 3) >> 2;
     g.nbc = (ux1 - g.ux0 + 3) >> 2;
     return g;
 }
 
-// Wave w of the tile: the 4 x 4 subtile (w / 2, w % 2); its block rows
+// Query c (row-major in its 4 x 4 subtile) of wave `wave` of the tile whose
+// first query is (y0, x0), before clamping to the map: the wave's loads, its
+// stores and large_wave_geometry all use this placement.
+struct QueryPos {
+    int y, x;
+};
+__host__ __device__ inline QueryPos large_query(int y0, int x0, int wave, int WX, int c)
+{
+    QueryPos q;
+    q.y = y0 + 4 * (wave / WX) + (c >> 2);
+    q.x = x0 + 4 * (wave % WX) + (c & 3);
+    return q;
+}
+
+// Wave w of the tile: the 4 x 4 subtile (w / WX, w % WX); its block rows
 // [rb0, rb1] and columns [cb0, cb0 + ncb) of the tile's union; colclamp:
 // some query's window is pushed in on the column axis.
 struct LargeWaveGeom {
@@ -179,12 +196,13 @@ struct LargeWaveGeom {
     int rb0, rb1, cb0, ncb;
 };
 __host__ __device__ inline LargeWaveGeom large_wave_geometry(const LargeTileGeom &t, int y0, int x0, int wave,
-                                                             int ks, int H, int W)
+                                                             int WX, int ks, int H, int W)
 {
     const int r = ks >> 1;
     LargeWaveGeom w;
-    w.ya = y0 + 4 * (wave >> 1);
-    w.xa = x0 + 4 * (wave & 1);
+    const QueryPos first = large_query(y0, x0, wave, WX, 0);
+    w.ya = first.y;
+    w.xa = first.x;
     w.active = w.ya < H && w.xa < W;
     const int yf = w.ya < H - 1 ? w.ya : H - 1, xf = w.xa < W - 1 ? w.xa : W - 1;
     const int yl = w.ya + 3 < H - 1 ? w.ya + 3 : H - 1, xl = w.xa + 3 < W - 1 ? w.xa + 3 : W - 1;
