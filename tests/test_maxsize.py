@@ -1,9 +1,10 @@
 """The largest problems the kernels address, checked on sampled outputs.
 
 - One map as large as 32-bit byte offsets inside a map allow (H*W*d*4 just
-  under 2^31: 4096 x 4095 at d = 32).
+  under 2^31: 4096 x 4095 at d = 32), on the halo kernel (k = 7) and the
+  wide-window kernel (k = 15).
 - A batch of more than 2^31 elements (80 x 16 maps of 256 x 256 x 32), so
-  that element offsets past 2^31 - 1 need 64 bits.
+  that element offsets past 2^31 - 1 need 64 bits, on both kernels.
 
 A sampled query is checked against the fp64 oracle run on a crop of the
 inputs: its window is the same in a crop of 2k rows and columns anchored to
@@ -77,11 +78,12 @@ def check_forward(q, k, v, rpb, ks, out, queries):
     return worst
 
 
-def test_forward_largest_map():
-    B, heads, H, W, d, ks = 1, 1, 4096, 4095, 32, 7
+@pytest.mark.parametrize("ks,dtype", [(7, torch.float16), (15, torch.float16)], ids=["halo-k7", "wide-window-k15"])
+def test_forward_largest_map(ks, dtype):
+    B, heads, H, W, d = 1, 1, 4096, 4095, 32
     assert 2 ** 31 - 2 ** 20 <= H * W * d * 4 < 2 ** 31
-    print("largest map", H, W, flush=True)
-    q, k, v = (draw((B, heads, H, W, d), torch.float16, s) for s in (1, 2, 3))
+    print("largest map", H, W, "k", ks, flush=True)
+    q, k, v = (draw((B, heads, H, W, d), dtype, s) for s in (1, 2, 3))
     rpb = draw((heads, 2 * ks - 1, 2 * ks - 1), torch.float32, 4)
     out = na2d.forward(q, k, v, rpb, ks)
     torch.cuda.synchronize()
@@ -93,12 +95,14 @@ def test_forward_largest_map():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("ks", [7, 13])
-def test_forward_past_2_31_elements(ks):
+@pytest.mark.parametrize("ks,dtype", [(7, torch.float16), (13, torch.float16), (13, torch.bfloat16),
+                                      (21, torch.bfloat16)],
+                         ids=["halo-k7", "halo-k13", "wide-window-k13-bf16", "wide-window-k21-bf16"])
+def test_forward_past_2_31_elements(ks, dtype):
     B, heads, H, W, d = 80, 16, 256, 256, 32
     assert B * heads * H * W * d > 2 ** 31
-    print("past 2^31 elements, k =", ks, flush=True)
-    q, k, v = (draw((B, heads, H, W, d), torch.float16, s) for s in (11, 12, 13))
+    print("past 2^31 elements, k =", ks, dtype, flush=True)
+    q, k, v = (draw((B, heads, H, W, d), dtype, s) for s in (11, 12, 13))
     rpb = draw((heads, 2 * ks - 1, 2 * ks - 1), torch.float32, 14)
     out = na2d.forward(q, k, v, rpb, ks)
     torch.cuda.synchronize()

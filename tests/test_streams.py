@@ -21,8 +21,9 @@ def _cases():
     return [
         ("2d persistent k7", (2, 2, 40, 36, 32), 7, "f16", lambda t, ks, s: na2d.forward(t["q"], t["k"], t["v"], t["rpb"], ks, stream=s)),
         ("2d ring k7", (1, 1, 136, 16, 32), 7, "f16", lambda t, ks, s: na2d.forward(t["q"], t["k"], t["v"], t["rpb"], ks, stream=s)),
-        ("2d halo k11", (1, 2, 30, 29, 32), 11, "bf16", lambda t, ks, s: na2d.forward(t["q"], t["k"], t["v"], t["rpb"], ks, stream=s)),
-        ("2d streaming k21", (1, 1, 45, 38, 32), 21, "bf16", lambda t, ks, s: na2d.forward(t["q"], t["k"], t["v"], t["rpb"], ks, stream=s)),
+        ("2d halo k11", (1, 2, 30, 29, 32), 11, "f16", lambda t, ks, s: na2d.forward(t["q"], t["k"], t["v"], t["rpb"], ks, stream=s)),
+        ("2d wide-window 8x8 tiles k21", (1, 1, 45, 38, 32), 21, "bf16", lambda t, ks, s: na2d.forward(t["q"], t["k"], t["v"], t["rpb"], ks, stream=s)),
+        ("2d wide-window 4x16 tiles k15", (1, 2, 37, 45, 32), 15, "f16", lambda t, ks, s: na2d.forward(t["q"], t["k"], t["v"], t["rpb"], ks, stream=s)),
         ("2d valu f32", (1, 2, 19, 17, 32), 5, "f32", lambda t, ks, s: na2d.forward(t["q"], t["k"], t["v"], t["rpb"], ks, stream=s)),
         ("sasa", (1, 2, 21, 19, 32), 7, "f16", lambda t, ks, s: na2d.forward_sasa2d(t["q"], t["k"], t["v"], t["rpb"], ks, stream=s)),
     ]
@@ -87,7 +88,8 @@ def test_two_streams_at_once():
 
 
 @pytest.mark.parametrize("ks,shape,dtype", [(7, (2, 2, 40, 36, 32), "f16"), (7, (1, 1, 136, 16, 32), "bf16"),
-                                            (21, (1, 1, 45, 38, 32), "bf16")], ids=str)
+                                            (21, (1, 1, 45, 38, 32), "bf16"), (13, (1, 2, 30, 29, 32), "bf16")],
+                         ids=str)
 def test_graph_replays(ks, shape, dtype):
     """Forward (with lse) and backward captured in one graph, replayed four
     times with fresh inputs copied in and eager work in between."""
