@@ -529,7 +529,8 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
     // streamed block at (y, xb): q and g rows of queries (y, xb + i), and the
     // softmax statistics of queries xb + 4 g + r (r = 0..3); zeros past the map
     struct Streamed {
-        u32x4 q, g0, g1, w01, w23;
+        u32x4 q, g0, g1;
+        unsigned w;
     };
     auto load_block = [&](int y, int xb) {
         Streamed t;
@@ -537,14 +538,15 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
         const unsigned goff = xb + c < W ? (unsigned)(y * W + xb + c) * 128u + 32u * g : kOutOfRange;
         t.g0 = __builtin_amdgcn_raw_buffer_load_b128(rg, goff, 0, 0);
         t.g1 = __builtin_amdgcn_raw_buffer_load_b128(rg, goff + 16u, 0, 0);
-        const unsigned woff = xb + 4 * g < W ? (unsigned)(y * W + xb + 4 * g) * 8u : kOutOfRange;
-        t.w01 = __builtin_amdgcn_raw_buffer_load_b128(rw, woff, 0, 0);
-        t.w23 = __builtin_amdgcn_raw_buffer_load_b128(rw, woff + 16u, 0, 0);
+        // lane (g, c < 8) fetches word c & 7 of queries xb + 4 g .. + 3 (their
+        // log-sum-exp and g . o pairs); process() broadcasts them across the row
+        const unsigned woff = xb + 4 * g < W ? (unsigned)(y * W + xb + 4 * g) * 8u + 4u * (c & 7) : kOutOfRange;
+        t.w = __builtin_amdgcn_raw_buffer_load_b32(rw, woff, 0, 0);
         return t;
     };
     auto process = [&](const Streamed &cur, int y, int xb) {
         {
-            const u32x4 qv = cur.q, g0 = cur.g0, g1 = cur.g1, w01 = cur.w01, w23 = cur.w23;
+            const u32x4 qv = cur.q, g0 = cur.g0, g1 = cur.g1;
             // q as A operand (the block's positions as rows), its copy for q^T
             *reinterpret_cast<u32x4 *>(qb + st_off) = qv;
             FragT gh, gl;
@@ -568,10 +570,16 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
             const floatx4 gvh = mfma16x16x32(gh, vf, floatx4{0, 0, 0, 0});
             const floatx4 gvl = mfma16x16x32(gl, vf, floatx4{0, 0, 0, 0});
             const floatx4 gv = gvh + gvl * LoScale<T>::down;
-            const float lse[4] = {__uint_as_float(w01[0]), __uint_as_float(w01[2]),
-                                  __uint_as_float(w23[0]), __uint_as_float(w23[2])};
-            const float dd[4] = {__uint_as_float(w01[1]), __uint_as_float(w01[3]),
-                                 __uint_as_float(w23[1]), __uint_as_float(w23[3])};
+            // row_newbcast:n (DPP control 0x150 + n): every lane of a 16-lane row takes lane n's word
+            const int wv = (int)cur.w;
+            const float lse[4] = {__int_as_float(__builtin_amdgcn_update_dpp(0, wv, 0x150, 0xf, 0xf, false)),
+                                  __int_as_float(__builtin_amdgcn_update_dpp(0, wv, 0x152, 0xf, 0xf, false)),
+                                  __int_as_float(__builtin_amdgcn_update_dpp(0, wv, 0x154, 0xf, 0xf, false)),
+                                  __int_as_float(__builtin_amdgcn_update_dpp(0, wv, 0x156, 0xf, 0xf, false))};
+            const float dd[4] = {__int_as_float(__builtin_amdgcn_update_dpp(0, wv, 0x151, 0xf, 0xf, false)),
+                                 __int_as_float(__builtin_amdgcn_update_dpp(0, wv, 0x153, 0xf, 0xf, false)),
+                                 __int_as_float(__builtin_amdgcn_update_dpp(0, wv, 0x155, 0xf, 0xf, false)),
+                                 __int_as_float(__builtin_amdgcn_update_dpp(0, wv, 0x157, 0xf, 0xf, false))};
             // p and dS for queries (y, xb + 4 g + r) and key c
             v4i16 ph, pl, sh, sl;
             const bool rowin = own_valid && (unsigned)(y - hy0) <= hyn;
