@@ -446,7 +446,8 @@ __global__ __launch_bounds__(kBT) void bwd_q_mfma_kernel(BArgs a)
 // drpb[h] += the tables of tiles [chunk * kRedRows, ...) of head h, for
 // job = chunk * heads + h (tiles are numbered map-major, map = b * heads + h).
 // Run by the first workgroups of the key pass, after the query pass wrote the
-// tables and cleared drpb.
+// tables and cleared drpb.  The 32 reads of an entry are issued together (one
+// memory latency before those workgroups start on their own tiles).
 __device__ inline void reduce_bias_tables(const BArgs &a, unsigned job)
 {
     const int nbb = (2 * a.ks - 1) * (2 * a.ks - 1);
@@ -455,7 +456,7 @@ __device__ inline void reduce_bias_tables(const BArgs &a, unsigned job)
     const int r0 = chunk * kRedRows;
     for (int e = threadIdx.x; e < nbb; e += kBT) {
         float acc = 0.f;
-#pragma unroll 8
+#pragma unroll
         for (int i = 0; i < kRedRows; ++i) {
             const int r = min(r0 + i, rows - 1);  // a row past the end is read but not added
             const int b = r / a.tiles_per_map, t = r - b * a.tiles_per_map;
