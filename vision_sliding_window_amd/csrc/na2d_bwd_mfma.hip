@@ -480,32 +480,33 @@ __global__ __launch_bounds__(kBT) void bwd_kv_mfma_kernel(BArgs a)
     const unsigned tile = xcd_tile(blockIdx.x, gridDim.x);
     if (tile >= a.ntiles) return;
     const Patch P = patch_of(a, tile);
-    const float *raw = stage_padded_bias(a, P.h, bias_lds, kKvPadL, kKvPadR);
-    __syncthreads();
-
     // the wave index is uniform: in a scalar register, loop bounds built on it stay scalar
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
     const int H = a.H, W = a.W, ks = a.ks, rs = 2 * ks - 1 + kKvPadL + kKvPadR;
     const int ky1 = P.y0 + 2 * wave;                 // the wave's key rows ky1, ky1 + 1
-    if (ky1 >= H) return;
+    // this lane's key (clamped into the map) and its k and v fragments, issued
+    // before the bias table is staged so that the two latencies overlap
     const int ky = min(ky1 + (c >> 3), H - 1), kx = min(P.x0 + (c & 7), W - 1);
+    const unsigned map_bytes = (unsigned)H * W * 64u;
+    const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, P.base, 64, map_bytes);
+    const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, P.base, 64, map_bytes);
+    const unsigned own_off = (unsigned)(ky * W + kx) * 64u + 16u * g;
+    const FragT kf = __builtin_bit_cast(FragT, __builtin_amdgcn_raw_buffer_load_b128(rk, own_off, 0, 0));
+    const FragT vf = __builtin_bit_cast(FragT, __builtin_amdgcn_raw_buffer_load_b128(rv, own_off, 0, 0));
+    const float *raw = stage_padded_bias(a, P.h, bias_lds, kKvPadL, kKvPadR);
+    __syncthreads();
+    if (ky1 >= H) return;
     const bool own_valid = ky1 + (c >> 3) < H && P.x0 + (c & 7) < W;
     // the queries whose windows hold this lane's key: rows hy0 .. hy1, columns hx0 .. hx1
     int hy0, hy1, hx0, hx1;
     holders(ky, ks, H, hy0, hy1);
     holders(kx, ks, W, hx0, hx1);
     const unsigned hyn = (unsigned)(hy1 - hy0), hxn = (unsigned)(hx1 - hx0);
-    const unsigned map_bytes = (unsigned)H * W * 64u;
     const __amdgpu_buffer_rsrc_t rq = map_rsrc(a.q, P.base, 64, map_bytes);
-    const __amdgpu_buffer_rsrc_t rk = map_rsrc(a.k, P.base, 64, map_bytes);
-    const __amdgpu_buffer_rsrc_t rv = map_rsrc(a.v, P.base, 64, map_bytes);
     const __amdgpu_buffer_rsrc_t rg = map_rsrc(a.dout, P.base, 128, (unsigned)H * W * 128u);
     const __amdgpu_buffer_rsrc_t rw = map_rsrc(a.ws, P.base, 8, (unsigned)H * W * 8u);
-    // the wave's own keys as B operands: lane (g, c) holds slice g of key c
-    const unsigned own_off = (unsigned)(ky * W + kx) * 64u + 16u * g;
-    const FragT kf = __builtin_bit_cast(FragT, __builtin_amdgcn_raw_buffer_load_b128(rk, own_off, 0, 0));
-    const FragT vf = __builtin_bit_cast(FragT, __builtin_amdgcn_raw_buffer_load_b128(rv, own_off, 0, 0));
+    // (kf, vf above: the wave's own keys as B operands, lane (g, c) holding slice g of key c)
 
     // the queries holding any of the wave's keys
     int ylo, yhi, xlo, xhi, t0, t1;
